@@ -1,0 +1,266 @@
+"""Benchmark of the hybrid local/global GQA attention path on one MI355X.
+
+Default workload: one full 52-layer decode step (three local layers then one
+global, repeated 13 times) at the maximum context of 131072 tokens, batch 4
+(independent sequences).  A step is, for every layer in order: append the new
+token's K/V to the layer cache and attend (split-K decode + merge), fused
+into one call per layer.  The 52
+layers run on one stream, captured once as a HIP graph and replayed.
+
+Printed: ONE JSON line.  ``value`` = KV bytes the step must read (every
+visible key of every layer, 1024 B per token per layer) / step time, in GB/s.
+``roofline`` covers the dominant kernel, the global-layer decode at 131072
+keys, timed with HIP events on the stream it is launched on.  ``cpu_baseline``
+is the fp64 oracle timed on this host on a bounded sample of the same
+workload.
+
+Inputs are synthetic: caches and queries are i.i.d. N(0,1) bf16 drawn from
+seeded generators on the GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+N_LAYERS = 52
+CTX = 131072
+
+
+def _ensure_built():
+    import global_gqa_attention_kv_amd as ga
+    if not os.path.exists(ga.library_path()):
+        from global_gqa_attention_kv_amd import build
+        build.build()
+    return ga
+
+
+def kv_bytes_step(kinds, positions):
+    """Algorithmic KV bytes of one decode step: each layer reads every
+    visible key's K and V for both KV heads (1024 B per token)."""
+    total = 0
+    for kind in kinds:
+        for p in positions:
+            keys = p + 1 if kind == 1 else min(p + 1, 2048)
+            total += keys * 1024
+    return total
+
+
+def build_decode_step(ga, torch, B, pos, seed=1003):
+    dev = torch.device("cuda")
+    kinds = [ga.layer_kind(l) for l in range(N_LAYERS)]
+    gen = torch.Generator(device=dev)
+    layers, qs, knews, vnews = [], [], [], []
+    for l, kind in enumerate(kinds):
+        gen.manual_seed(seed * 1000 + l)
+        cap = ga.WINDOW if kind == ga.LOCAL else CTX
+        shape = (B, cap, ga.HKV, ga.D)
+        k = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+        layers.append(ga.Layer(kind, k, v))
+        qs.append(torch.randn((B, ga.HQ, ga.D), generator=gen,
+                              device=dev).to(torch.bfloat16))
+        knews.append(torch.randn((B, 1, ga.HKV, ga.D), generator=gen,
+                                 device=dev).to(torch.bfloat16))
+        vnews.append(torch.randn((B, 1, ga.HKV, ga.D), generator=gen,
+                                 device=dev).to(torch.bfloat16))
+    ws = torch.zeros(max(ga.workspace_bytes(ga.OP_DECODE, k, B, 1, CTX)
+                         for k in (ga.LOCAL, ga.GLOBAL)),
+                     dtype=torch.uint8, device=dev)
+    outs = [torch.empty((B, ga.HQ, ga.D), dtype=torch.float32, device=dev)
+            for _ in kinds]
+    positions = [pos] * B
+
+    def step():
+        for l in range(N_LAYERS):
+            ga.attn_decode_append(layers[l], qs[l], knews[l], vnews[l],
+                                  positions, outs[l], ws)
+
+    def step_kind(kind):
+        def f():
+            for l in range(N_LAYERS):
+                if kinds[l] == kind:
+                    ga.attn_decode_append(layers[l], qs[l], knews[l],
+                                          vnews[l], positions, outs[l], ws)
+        return f
+
+    step.local_only = step_kind(ga.LOCAL)
+    step.global_only = step_kind(ga.GLOBAL)
+    return kinds, layers, qs, outs, ws, positions, step
+
+
+def time_graph(torch, fn, steps, warmup):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager run once before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, g
+
+
+def time_global_decode(ga, torch, layers, qs, outs, ws, positions, kinds,
+                       reps):
+    """Average duration of one global-layer decode call (split kernel +
+    merge kernel) at the step's context, rotating over the 13 global layers
+    so the 256 MB last-level cache cannot serve repeats."""
+    glob = [l for l, k in enumerate(kinds) if k == ga.GLOBAL]
+    for l in glob:
+        ga.attn_decode(layers[l], qs[l], positions, outs[l], ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    n = 0
+    for _ in range(reps):
+        for l in glob:
+            ga.attn_decode(layers[l], qs[l], positions, outs[l], ws)
+            n += 1
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def cpu_baseline(ga, torch, layers, qs, positions, kinds, budget_s=20.0):
+    """The fp64 oracle on this host: one decode step for sequence 0 over as
+    many layers (in step order) as fit the time budget."""
+    import numpy as np
+    import oracle
+    import synth_inputs as si
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    p = positions[0]
+    done_bytes, done_layers = 0, 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    for l, kind in enumerate(kinds):
+        lo = 0 if kind == ga.GLOBAL else max(0, p - ga.WINDOW + 1)
+        if kind == ga.GLOBAL:
+            kb = si.bits(layers[l].k[0, lo:p + 1])
+            vb = si.bits(layers[l].v[0, lo:p + 1])
+        else:
+            idx = torch.arange(lo, p + 1, device=layers[l].k.device) % ga.WINDOW
+            kb = si.bits(layers[l].k[0, idx])
+            vb = si.bits(layers[l].v[0, idx])
+        qb = si.bits(qs[l][0:1])
+        ts = time.perf_counter()
+        oracle.attend(qb, [p], kb, vb, lo, hq=32, hkv=2, d=128,
+                      window=ga.WINDOW if kind == ga.LOCAL else 0,
+                      rope=kind == ga.LOCAL, nthreads=cores)
+        elapsed += time.perf_counter() - ts
+        done_bytes += (p + 1 - lo) * 1024
+        done_layers += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    return {
+        "value": round(done_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "fp64 oracle, one decode step of sequence 0 at context %d "
+                  "over the first %d of 52 layers (%.1f MB of KV), %.2f s of "
+                  "oracle time" % (p + 1, done_layers, done_bytes / 1e6,
+                                   elapsed),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the attention path has no "
+              "multi-GPU execution (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    ga = _ensure_built()
+    torch.cuda.set_device(0)
+    B = args.batch
+    pos = CTX - 1
+    kinds, layers, qs, outs, ws, positions, step = build_decode_step(
+        ga, torch, B, pos)
+    torch.cuda.synchronize()
+    print("# setup done: %d layers, batch %d, context %d" % (N_LAYERS, B, CTX),
+          file=sys.stderr, flush=True)
+
+    ms, _graph = time_graph(torch, step, args.steps, args.warmup)
+    kvb = kv_bytes_step(kinds, positions)
+    value = kvb / (ms * 1e-3) / 1e9
+
+    ms_local, _ = time_graph(torch, step.local_only, args.steps, args.warmup)
+    ms_global, _ = time_graph(torch, step.global_only, args.steps, args.warmup)
+
+    kms = time_global_decode(ga, torch, layers, qs, outs, ws, positions,
+                             kinds, args.kernel_reps)
+    kbytes = B * (pos + 1) * 1024
+    achieved = kbytes / (kms * 1e-3) / 1e9
+
+    line = {
+        "metric": "decode attn KV GB/s (% HBM peak) at 131K ctx",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "52-layer decode step (39 local W=2048 RoPE + "
+                               "13 global), context 131072, append + attend "
+                               "per layer, HIP graph",
+                   "global_batch": B, "seq_len": CTX,
+                   "parallelism": "none (1 GPU)"},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "breakdown_ms": {"39 local layers": round(ms_local, 4),
+                         "13 global layers": round(ms_global, 4)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "global-layer decode call (split-K kernel + merge "
+                      "kernel), %d keys x batch %d" % (pos + 1, B),
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_ms": round(kms, 5),
+            "algorithmic_bytes": kbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(ga, torch, layers, qs, positions,
+                                            kinds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,232 @@
+"""Python binding of libgqa_attn.so: grouped-query attention (32 query heads,
+2 KV heads, head dim 128) with a hybrid local / global KV cache on MI355X.
+
+This module only marshals arguments: it checks tensor placement, dtype and
+shape, then calls the C ABI declared in ``include/gqa_attn.h`` with raw device
+pointers and the current HIP stream.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback.  If the library has not been
+built, importing works but the first call raises :class:`LibraryMissing`.
+
+PyTorch provides device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "LOCAL", "GLOBAL", "OP_DECODE", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
+    "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
+    "attn_decode", "attn_decode_append", "workspace_bytes", "workspace", "status_string", "abi_version",
+    "library_path", "layer_kind",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libgqa_attn.so")
+
+LOCAL, GLOBAL = 0, 1
+OP_DECODE = 0
+HQ, HKV, D, WINDOW, MAX_CONTEXT, MAX_BATCH = 32, 2, 128, 2048, 131072, 64
+ROPE_THETA = 10000.0
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s failed: %s (%d)" % (what, status_string(status),
+                                                 status))
+        self.status = status
+
+
+class _CLayer(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("capacity", ctypes.c_int64), ("rope_theta", ctypes.c_double),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("seq_stride", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(
+                "libgqa_attn.so is not built; run "
+                "`python -m global_gqa_attention_kv_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        p, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L = ctypes.POINTER(_CLayer)
+        lib.gqa_abi_version.restype = i32
+        lib.gqa_status_string.restype = ctypes.c_char_p
+        lib.gqa_status_string.argtypes = [i32]
+        lib.gqa_workspace_bytes.restype = ctypes.c_size_t
+        lib.gqa_workspace_bytes.argtypes = [i32, i32, i32, i32, i64]
+        lib.gqa_kv_append.restype = i32
+        lib.gqa_kv_append.argtypes = [L, p, p, p, i32, i32, p]
+        lib.gqa_attn_decode.restype = i32
+        lib.gqa_attn_decode.argtypes = [L, p, p, i32, p, p, ctypes.c_size_t, p]
+        lib.gqa_attn_decode_append.restype = i32
+        lib.gqa_attn_decode_append.argtypes = [L, p, p, p, p, i32, p, p,
+                                               ctypes.c_size_t, p]
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return _load().gqa_abi_version()
+
+
+def status_string(status: int) -> str:
+    return _load().gqa_status_string(int(status)).decode()
+
+
+def workspace_bytes(op: int, kind: int, B: int, n: int, max_ctx: int) -> int:
+    return int(_load().gqa_workspace_bytes(op, kind, B, n, int(max_ctx)))
+
+
+def layer_kind(layer_index: int) -> int:
+    """Three local layers then one global layer, repeating."""
+    return GLOBAL if layer_index % 4 == 3 else LOCAL
+
+
+class Layer:
+    """One attention layer's K/V cache, held in caller-owned torch tensors.
+
+    k, v: bf16 [B, capacity, 2, 128] on the GPU.  Local layers have capacity
+    2048 (a ring, slot = position mod 2048) and RoPE base ``rope_theta``;
+    global layers have capacity up to 131072 (slot = position) and no RoPE."""
+
+    def __init__(self, kind, k, v, rope_theta=None):
+        self.kind = int(kind)
+        self.k = k
+        self.v = v
+        if rope_theta is None:
+            rope_theta = ROPE_THETA if self.kind == LOCAL else 0.0
+        self.rope_theta = float(rope_theta)
+        assert k.shape == v.shape and k.dim() == 4
+        self.batch, self.capacity = int(k.shape[0]), int(k.shape[1])
+        self._c = _CLayer(self.kind, WINDOW if self.kind == LOCAL else 0,
+                          self.capacity, self.rope_theta, k.data_ptr(),
+                          v.data_ptr(), int(k.stride(0)))
+        if k.stride(0) != v.stride(0):
+            raise ValueError("k and v must share the sequence stride")
+
+    @classmethod
+    def allocate(cls, kind, batch, capacity=None, device="cuda", fill=None):
+        if capacity is None:
+            capacity = WINDOW if kind == LOCAL else MAX_CONTEXT
+        shape = (batch, capacity, HKV, D)
+        if fill is None:
+            k = torch.empty(shape, dtype=torch.bfloat16, device=device)
+            v = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        else:
+            k = torch.full(shape, fill, dtype=torch.bfloat16, device=device)
+            v = torch.full(shape, fill, dtype=torch.bfloat16, device=device)
+        return cls(kind, k, v)
+
+    @property
+    def c_ref(self):
+        return ctypes.byref(self._c)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t, dtype, shape, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape),
+                                                             tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _positions(pos, B):
+    arr = (ctypes.c_int64 * B)()
+    vals = pos.tolist() if isinstance(pos, torch.Tensor) else list(pos)
+    if len(vals) != B:
+        raise ValueError("need %d positions, got %d" % (B, len(vals)))
+    for i, x in enumerate(vals):
+        arr[i] = int(x)
+    return arr
+
+
+def kv_append(layer: Layer, k_new, v_new, pos0, stream=None):
+    """Write n new tokens per sequence into the layer cache.
+    k_new, v_new: bf16 [B, n, 2, 128]; pos0: B host positions."""
+    B, n = int(k_new.shape[0]), int(k_new.shape[1])
+    kp = _dev(k_new, torch.bfloat16, (B, n, HKV, D), "k_new")
+    vp = _dev(v_new, torch.bfloat16, (B, n, HKV, D), "v_new")
+    rc = _load().gqa_kv_append(layer.c_ref, kp, vp, _positions(pos0, B), B, n,
+                               _stream(stream))
+    if rc != 0:
+        raise GqaError(rc, "gqa_kv_append")
+
+
+def workspace(op, kind, B, n, max_ctx, device="cuda"):
+    """A zero-filled workspace tensor for the given operation and shape."""
+    need = workspace_bytes(op, kind, B, n, max_ctx)
+    if need == 0:
+        raise ValueError("invalid workspace request")
+    return torch.zeros(need, dtype=torch.uint8, device=device)
+
+
+def _decode_common(fn, name, layer, q, pos, out, ws, stream, extra=()):
+    B = int(q.shape[0])
+    qp = _dev(q, torch.bfloat16, (B, HQ, D), "q")
+    if out is None:
+        out = torch.empty((B, HQ, D), dtype=torch.float32, device=q.device)
+    op = _dev(out, torch.float32, (B, HQ, D), "out")
+    posc = _positions(pos, B)
+    if ws is None:
+        ws = workspace(OP_DECODE, layer.kind, B, 1,
+                       max(int(x) for x in posc) + 1, device=q.device)
+    wp = _dev(ws, ws.dtype, None, "ws")
+    args = (layer.c_ref, qp) + tuple(extra) + (posc, B, op, wp,
+                                               ws.numel() * ws.element_size(),
+                                               _stream(stream))
+    rc = fn(*args)
+    if rc != 0:
+        raise GqaError(rc, name)
+    return out
+
+
+def attn_decode(layer: Layer, q, pos, out=None, ws=None, stream=None):
+    """One decode step.  q: bf16 [B, 32, 128]; pos: B host positions of the
+    query tokens (already appended).  ws: zero-filled workspace (see
+    :func:`workspace`), allocated per call when omitted.
+    Returns out: fp32 [B, 32, 128]."""
+    return _decode_common(_load().gqa_attn_decode, "gqa_attn_decode", layer,
+                          q, pos, out, ws, stream)
+
+
+def attn_decode_append(layer: Layer, q, k_new, v_new, pos, out=None, ws=None,
+                       stream=None):
+    """Append the new token (k_new, v_new: bf16 [B, 1, 2, 128]) at pos and
+    attend, in one launch.  Returns out: fp32 [B, 32, 128]."""
+    B = int(q.shape[0])
+    kp = _dev(k_new, torch.bfloat16, (B, 1, HKV, D), "k_new")
+    vp = _dev(v_new, torch.bfloat16, (B, 1, HKV, D), "v_new")
+    return _decode_common(_load().gqa_attn_decode_append,
+                          "gqa_attn_decode_append", layer, q, pos, out, ws,
+                          stream, extra=(kp, vp))

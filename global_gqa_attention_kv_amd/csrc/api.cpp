@@ -1,0 +1,177 @@
+// api.cpp -- the extern "C" entry points of libgqa_attn.so (see
+// include/gqa_attn.h).  Each call validates on the host, fills a kernel
+// parameter block and enqueues on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "internal.h"
+#include "validate.h"
+
+namespace gqa {
+
+namespace {
+// Wide decode launches aim for about this many workgroups so every compute
+// unit holds a few resident workgroups; each workgroup then streams several
+// tiles.
+constexpr int kDecodeTargetWGs = 768;
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+DecodePlan plan_decode(int kind, int B, int64_t max_keys) {
+  const int64_t tiles = (max_keys + kDecTile - 1) / kDecTile;
+  DecodePlan p;
+  if (kind == GQA_LOCAL) {
+    p.narrow = true;
+    p.heads_per_wg = 4;
+    p.head_groups = kGroup / 4;
+    // one tile per workgroup for a single sequence (latency-bound); two
+    // for larger batches so every workgroup of the launch is resident at once
+    p.tiles_per_split = B >= 2 ? 2 : 1;
+    p.splits = (int)((tiles + p.tiles_per_split - 1) / p.tiles_per_split);
+    if (p.splits < 1) p.splits = 1;
+    return p;
+  }
+  p.narrow = false;
+  p.heads_per_wg = kGroup;
+  p.head_groups = 1;
+  int64_t want = (kDecodeTargetWGs + 2 * B - 1) / (2 * B);
+  if (want < 1) want = 1;
+  int64_t per = (tiles + want - 1) / want;
+  if (per < 1) per = 1;
+  p.tiles_per_split = (int)per;
+  p.splits = (int)((tiles + per - 1) / per);
+  if (p.splits < 1) p.splits = 1;
+  return p;
+}
+
+// Workspace: partial sums [B][2][head_groups][splits][heads_per_wg x 130]
+// floats, then one int32 counter per (sequence, KV head, head group).
+size_t decode_ws_bytes(int B, const DecodePlan& plan) {
+  const size_t parts = (size_t)B * kHkv * plan.head_groups * plan.splits *
+                       part_floats(plan) * sizeof(float);
+  return align256(parts) + align256((size_t)B * kHkv * plan.head_groups * 4);
+}
+
+}  // namespace gqa
+
+using namespace gqa;
+
+extern "C" {
+
+int gqa_abi_version(void) { return GQA_ABI_VERSION; }
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_POS_RANGE: return "position out of range";
+    case GQA_ERR_MISALIGNED: return "pointer or stride not 16-byte aligned";
+    case GQA_ERR_WS_TOO_SMALL: return "workspace too small";
+    case GQA_ERR_UNSUPPORTED: return "layer outside the compiled shape";
+    case GQA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx) {
+  if (B < 1 || B > GQA_MAX_BATCH || n < 1 || max_ctx < 1) return 0;
+  if (kind != GQA_LOCAL && kind != GQA_GLOBAL) return 0;
+  if (kind == GQA_GLOBAL && max_ctx > GQA_MAX_CONTEXT) return 0;
+  switch (op) {
+    case GQA_OP_DECODE: {
+      const int64_t keys = visible_keys(kind, max_ctx - 1);
+      return decode_ws_bytes(B, plan_decode(kind, B, keys));
+    }
+    default:
+      return 0;
+  }
+}
+
+int gqa_kv_append(const gqa_layer* layer, const void* k_new, const void* v_new,
+                  const int64_t* pos0, int B, int n, void* stream) {
+  int rc = check_append(layer, k_new, v_new, pos0, B, n);
+  if (rc != GQA_OK) return rc;
+  AppendParams p;
+  memset(&p, 0, sizeof p);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k = static_cast<uint16_t*>(layer->k);
+  p.v = static_cast<uint16_t*>(layer->v);
+  p.seq_stride = layer->seq_stride;
+  p.capacity = layer->capacity;
+  p.n = n;
+  p.local = layer->kind == GQA_LOCAL;
+  p.first = (p.local && n > kW) ? n - kW : 0;
+  for (int b = 0; b < B; ++b) p.pos0[b] = pos0[b];
+  const int count = n - p.first;
+  hipError_t e = launch_kv_append(p, B, count, (hipStream_t)stream);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+static int decode_impl(const gqa_layer* layer, const void* q,
+                       const void* k_new, const void* v_new,
+                       const int64_t* pos, int B, float* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int64_t max_keys = 0;
+  int rc = check_decode(layer, q, pos, B, out, &max_keys);
+  if (rc != GQA_OK) return rc;
+  if (k_new || v_new) {
+    if (!k_new || !v_new) return GQA_ERR_INVALID_ARG;
+    if (((uintptr_t)k_new & 15u) || ((uintptr_t)v_new & 15u))
+      return GQA_ERR_MISALIGNED;
+  }
+  const DecodePlan plan = plan_decode(layer->kind, B, max_keys);
+  const size_t need = decode_ws_bytes(B, plan);
+  if (!ws) return GQA_ERR_INVALID_ARG;
+  if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
+  if (ws_bytes < need) return GQA_ERR_WS_TOO_SMALL;
+  DecodeParams p;
+  memset(&p, 0, sizeof p);
+  p.k = static_cast<const uint16_t*>(layer->k);
+  p.k_mut = static_cast<uint16_t*>(layer->k);
+  p.v = static_cast<const uint16_t*>(layer->v);
+  p.v_mut = static_cast<uint16_t*>(layer->v);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.q = static_cast<const uint32_t*>(q);
+  const size_t parts = (size_t)B * kHkv * plan.head_groups * plan.splits *
+                       part_floats(plan) * sizeof(float);
+  p.part = static_cast<float*>(ws);
+  p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                          align256(parts));
+  p.out = out;
+  p.seq_stride = layer->seq_stride;
+  p.scale_log2 = (float)(1.0 / sqrt((double)kD) * 1.4426950408889634);
+  p.splits = plan.splits;
+  p.tiles_per_split = plan.tiles_per_split;
+  p.units = B * kHkv * plan.splits;
+  const bool local = layer->kind == GQA_LOCAL;
+  if (local) {
+    // revolutions per position of frequency c: theta^(-c/64) / (2 pi),
+    // evaluated in double and rounded once.
+    for (int c = 0; c < kD / 2; ++c)
+      p.rope_rev[c] = (float)(pow(layer->rope_theta, -(double)c / (kD / 2)) /
+                              (2.0 * 3.14159265358979323846));
+  }
+  for (int b = 0; b < B; ++b) p.pos[b] = pos[b];
+  hipError_t e = launch_decode(p, plan, local, B, (hipStream_t)stream);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_attn_decode(const gqa_layer* layer, const void* q, const int64_t* pos,
+                    int B, float* out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  return decode_impl(layer, q, nullptr, nullptr, pos, B, out, ws, ws_bytes,
+                     stream);
+}
+
+int gqa_attn_decode_append(const gqa_layer* layer, const void* q,
+                           const void* k_new, const void* v_new,
+                           const int64_t* pos, int B, float* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!k_new || !v_new) return GQA_ERR_INVALID_ARG;
+  return decode_impl(layer, q, k_new, v_new, pos, B, out, ws, ws_bytes,
+                     stream);
+}
+
+}  // extern "C"

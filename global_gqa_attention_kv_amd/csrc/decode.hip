@@ -1,0 +1,547 @@
+// decode.hip -- split-K flash-decode for one query token per sequence.
+//
+// What is computed (pages "Deep dive into Muse Glimmer", shishifenxi.com,
+// section 01, and "Tomas Koutsky explains how Meta fits Muse Glimmer into
+// 24 GB", runtimewire.com, "Narrow cache" / "Long context still costs
+// compute"): for each sequence b and query head h, softmax(q.k_j / sqrt(128))
+// weighted sum of v_j over the visible keys of KV head h/16 -- all positions
+// 0..p on a global layer, positions p-2047..p through the 2048-slot ring with
+// RoPE on a local layer.
+//
+// Design (gfx950, VALU; decode is a streaming read of the cache):
+//  * One workgroup of 256 threads owns one (sequence, KV head, key split) and
+//    serves all 16 query heads of that KV head, so each cached K/V byte is
+//    fetched from HBM exactly once.
+//  * Keys stream through LDS in tiles of 64.  Every thread prefetches its
+//    share of the next tile with 16-byte coalesced loads while the current
+//    tile is being consumed.  K rows are stored with an XOR swizzle of their
+//    16-byte chunks so a lane can read a whole row without bank conflicts; V
+//    is re-packed into (key 2i, key 2i+1) bf16 pairs on the way in so the P.V
+//    product can use the packed-pair dot instruction.
+//  * Q.K: lane = key, each wave takes 4 of the 16 heads; the query words are
+//    wave-uniform and come straight from the scalar cache as SGPR operands of
+//    v_dot2_f32_bf16 (bf16 products exact, fp32 accumulation).
+//  * Online softmax in the log2 domain with a lazy maximum: the running
+//    maximum is only raised (and the accumulators rescaled) when some score
+//    exceeds it by more than 2^8, which keeps every exponent <= 2^8 while
+//    skipping nearly all cross-lane reductions.
+//  * P.V: each wave accumulates its 4 heads x 128 dims; lane = (8 dims, one
+//    of 4 key-pair groups); P is stored to wave-private LDS as bf16 pairs.
+//  * Local layers rotate each key by its offset to the query (j - i) before
+//    it reaches LDS; since <R_i q, R_j k> = <q, R_{j-i} k> the query stays
+//    unrotated and the angles stay small (|j - i| < 2048), so fp32 angle
+//    arithmetic keeps ~1e-4 rad accuracy.
+//  * Each workgroup writes (m, l, o) for its split.  Global layers (large
+//    caches) use the 16-head shape above and a second, fully parallel merge
+//    kernel.  Local layers (2048 keys, latency-bound) use a narrow shape: 4
+//    heads (one per wave) and one tile per workgroup, the four head groups of
+//    a tile placed on one XCD so they share its L2, and the last workgroup of
+//    each (sequence, KV head, head group) -- found with a device-scope
+//    counter in the workspace -- merges the splits in the same launch.  The
+//    partials travel with device-scope (write-through) stores and loads, so
+//    no workgroup has to write back its whole L2.
+//  * Optionally the call appends the query's own K/V: the kernel reads that
+//    key from the new-token buffers and one workgroup stores it to its slot,
+//    saving a separate append launch per layer.
+#include "device_common.h"
+#include "internal.h"
+
+namespace gqa {
+
+namespace {
+
+constexpr float kTau = 8.0f;  // lazy-rescale threshold in log2 units
+constexpr int kKsBytes = kDecTile * 256;        // 64 rows x 256 B
+constexpr int kVsBytes = (kDecTile / 2) * 512;  // 32 key pairs x 128 words
+
+__device__ __forceinline__ int64_t slot_of(int64_t position, bool local) {
+  return local ? (position & (kW - 1)) : position;
+}
+
+// Rotate the 8 dims (d, d+64) held in lo/hi by `delta` positions.
+__device__ __forceinline__ void rope_rotate(uint4& lo, uint4& hi, float delta,
+                                            const float* rev) {
+  uint32_t* l = reinterpret_cast<uint32_t*>(&lo);
+  uint32_t* h = reinterpret_cast<uint32_t*>(&hi);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = bf16_lo(l[e]), x1 = bf16_hi(l[e]);
+    const float y0 = bf16_lo(h[e]), y1 = bf16_hi(h[e]);
+    float r0 = delta * rev[2 * e], r1 = delta * rev[2 * e + 1];
+    r0 -= rintf(r0);
+    r1 -= rintf(r1);
+    float s0, c0, s1, c1;
+    sincos_rev(r0, &s0, &c0);
+    sincos_rev(r1, &s1, &c1);
+    l[e] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+    h[e] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+  }
+}
+
+template <bool LOCAL, int HW, bool FUSED>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(
+    const DecodeParams p) {
+  constexpr int HG = 4 / HW;              // head groups per KV head
+  constexpr int HPW = 4 * HW;             // query heads per workgroup
+  constexpr int PF = HPW * (kD + 2);      // floats of one partial
+  constexpr int kPsWave = (kDecTile / 2) * HW * 4;
+  __shared__ __attribute__((aligned(16)))
+  uint8_t smem[kKsBytes + kVsBytes + 4 * kPsWave];
+  __shared__ int s_ticket;
+  uint8_t* Ks = smem;
+  uint8_t* Vs = smem + kKsBytes;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint8_t* Ps = smem + kKsBytes + kVsBytes + w * kPsWave;
+
+  // workgroup -> (unit, head group).  Consecutive workgroup ids go to
+  // different XCDs round-robin, so the HG workgroups of one unit are placed
+  // 8 ids apart: same XCD, same L2, dispatched together.
+  int unit, hg;
+  if (HG == 1) {
+    unit = blockIdx.x;
+    hg = 0;
+  } else {
+    const int r = blockIdx.x % (8 * HG);
+    unit = (blockIdx.x / (8 * HG)) * 8 + (r & 7);
+    hg = r >> 3;
+  }
+  if (unit >= p.units) return;  // padding of the XCD-aware grid
+  const int split = unit % p.splits;
+  const int bg = unit / p.splits;  // b * 2 + g
+  const int g = bg % kHkv;
+  const int b = bg / kHkv;
+
+  const int64_t pos = p.pos[b];
+  const int64_t j_first = LOCAL ? (pos > kW - 1 ? pos - (kW - 1) : 0) : 0;
+  const int nkeys = (int)(pos - j_first + 1);
+  const int span = p.tiles_per_split * kDecTile;
+  const int k_begin = split * span;
+  const int k_end = min(nkeys, k_begin + span);
+  const bool has_keys = k_begin < nkeys;
+  const int new_key = nkeys - 1;          // key index of the query's own token
+  const bool use_new = p.k_new != nullptr;
+  float* const part_base = p.part + (size_t)(bg * HG + hg) * p.splits * PF;
+  float* const part = part_base + (size_t)split * PF;
+
+  // The call appends the query's own token: one workgroup writes it to its
+  // slot, which no other workgroup reads in this launch (they take that key
+  // from k_new / v_new).
+  if (use_new && g == 0 && hg == 0 && has_keys && new_key / span == split &&
+      tid < 64) {
+    const bool is_v = tid >= 32;
+    const int chunk = tid & 31;
+    const uint16_t* src = (is_v ? p.v_new : p.k_new) +
+                          (int64_t)b * kTokenElems + chunk * 8;
+    uint16_t* dst = (is_v ? p.v_mut : p.k_mut) + (int64_t)b * p.seq_stride +
+                    slot_of(pos, LOCAL) * kTokenElems + chunk * 8;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+
+  if (has_keys) {
+    const int ntiles = (k_end - k_begin + kDecTile - 1) / kDecTile;
+    const uint16_t* Kb = p.k + (int64_t)b * p.seq_stride + g * kD;
+    const uint16_t* Vb = p.v + (int64_t)b * p.seq_stride + g * kD;
+    const uint16_t* Kn = p.k_new + (int64_t)b * kTokenElems + g * kD;
+    const uint16_t* Vn = p.v_new + (int64_t)b * kTokenElems + g * kD;
+    const int head0 = g * kGroup + hg * HPW + w * HW;  // this wave's heads
+    // The query never changes during the kernel: reading it through the
+    // constant address space lets the compiler use scalar loads (SGPR
+    // operands) for these wave-uniform words.
+    const __attribute__((address_space(4))) uint32_t* qw =
+        (const __attribute__((address_space(4))) uint32_t*)(
+            p.q + ((int64_t)b * kHq + head0) * (kD / 2));
+
+    uint4 kreg[2][2];  // [unit][dims 8c..8c+7 | 8c+64..8c+71]
+    uint4 vreg[2][2];  // [unit][key 2r | key 2r+1]
+
+    auto key_row = [&](const uint16_t* base, const uint16_t* fresh, int key) {
+      return (use_new && key == new_key)
+                 ? fresh
+                 : base + slot_of(j_first + key, LOCAL) * kTokenElems;
+    };
+    auto load_tile = [&](int t) {
+      const int kb = k_begin + t * kDecTile;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = tid + i * kDecThreads;
+        const int row = u >> 3, cp = u & 7;
+        const int key = min(kb + row, k_end - 1);
+        const uint16_t* src = key_row(Kb, Kn, key) + cp * 8;
+        kreg[i][0] = *reinterpret_cast<const uint4*>(src);
+        kreg[i][1] = *reinterpret_cast<const uint4*>(src + 64);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = tid + i * kDecThreads;
+        const int rp = u >> 4, c = u & 15;
+        const int ka = min(kb + 2 * rp, k_end - 1);
+        const int kc = min(kb + 2 * rp + 1, k_end - 1);
+        vreg[i][0] =
+            *reinterpret_cast<const uint4*>(key_row(Vb, Vn, ka) + c * 8);
+        vreg[i][1] =
+            *reinterpret_cast<const uint4*>(key_row(Vb, Vn, kc) + c * 8);
+      }
+    };
+
+    auto store_tile = [&](int t) {
+      const int kb = k_begin + t * kDecTile;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = tid + i * kDecThreads;
+        const int row = u >> 3, cp = u & 7;
+        uint4 lo = kreg[i][0], hi = kreg[i][1];
+        if (LOCAL) {
+          const int key = min(kb + row, k_end - 1);
+          rope_rotate(lo, hi, (float)(j_first + key - pos),
+                      p.rope_rev + cp * 8);
+        }
+        *reinterpret_cast<uint4*>(Ks + row * 256 + ((cp ^ (row & 15)) << 4)) =
+            lo;
+        *reinterpret_cast<uint4*>(Ks + row * 256 +
+                                  (((cp + 8) ^ (row & 15)) << 4)) = hi;
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = tid + i * kDecThreads;
+        const int rp = u >> 4, c = u & 15;
+        const uint4 a = vreg[i][0], e = vreg[i][1];
+        uint4 o0, o1;
+        o0.x = interleave_lo(a.x, e.x);
+        o0.y = interleave_hi(a.x, e.x);
+        o0.z = interleave_lo(a.y, e.y);
+        o0.w = interleave_hi(a.y, e.y);
+        o1.x = interleave_lo(a.z, e.z);
+        o1.y = interleave_hi(a.z, e.z);
+        o1.z = interleave_lo(a.w, e.w);
+        o1.w = interleave_hi(a.w, e.w);
+        *reinterpret_cast<uint4*>(Vs + rp * 512 + c * 32) = o0;
+        *reinterpret_cast<uint4*>(Vs + rp * 512 + c * 32 + 16) = o1;
+      }
+    };
+
+    float m[HW], lsum[HW], o[HW][8];
+#pragma unroll
+    for (int hl = 0; hl < HW; ++hl) {
+      m[hl] = -INFINITY;
+      lsum[hl] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hl][e] = 0.0f;
+    }
+    const int dg = lane & 15, kg = lane >> 4;
+
+    load_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+      store_tile(t);
+      __syncthreads();
+      if (t + 1 < ntiles) load_tile(t + 1);
+
+      // ---- scores: lane = key of this tile, HW heads per wave
+      float acc[HW];
+#pragma unroll
+      for (int hl = 0; hl < HW; ++hl) acc[hl] = 0.0f;
+      const uint8_t* krow = Ks + lane * 256;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const uint4 kc =
+            *reinterpret_cast<const uint4*>(krow + ((c ^ (lane & 15)) << 4));
+#pragma unroll
+        for (int hl = 0; hl < HW; ++hl) {
+          const __attribute__((address_space(4))) uint32_t* qr =
+              qw + hl * (kD / 2) + c * 4;
+          acc[hl] = dot2_bf16(qr[0], kc.x, acc[hl]);
+          acc[hl] = dot2_bf16(qr[1], kc.y, acc[hl]);
+          acc[hl] = dot2_bf16(qr[2], kc.z, acc[hl]);
+          acc[hl] = dot2_bf16(qr[3], kc.w, acc[hl]);
+        }
+      }
+      const bool valid = k_begin + t * kDecTile + lane < k_end;
+      float s2[HW];
+      bool need = false;
+#pragma unroll
+      for (int hl = 0; hl < HW; ++hl) {
+        s2[hl] = valid ? acc[hl] * p.scale_log2 : -INFINITY;
+        need |= s2[hl] > m[hl] + kTau;
+      }
+      if (__any(need)) {  // wave-uniform: raise the running maximum
+#pragma unroll
+        for (int hl = 0; hl < HW; ++hl) {
+          const float mn = fmaxf(m[hl], wave_max(s2[hl]));
+          const float alpha = fast_exp2(m[hl] - mn);
+          m[hl] = mn;
+          lsum[hl] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[hl][e] *= alpha;
+        }
+      }
+      uint16_t* P16 = reinterpret_cast<uint16_t*>(Ps);
+#pragma unroll
+      for (int hl = 0; hl < HW; ++hl) {
+        // the denominator sums exactly the bf16 weights the P.V product
+        // uses, so the weights of every output sum to one
+        const uint16_t pb = to_bf16(fast_exp2(s2[hl] - m[hl]));
+        lsum[hl] += __builtin_bit_cast(float, (uint32_t)pb << 16);
+        P16[(lane >> 1) * (2 * HW) + hl * 2 + (lane & 1)] = pb;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P visible to the wave
+      __builtin_amdgcn_wave_barrier();
+
+      // ---- P.V: lane = (8 dims, key-pair group)
+#pragma unroll
+      for (int i = 0; i < kDecTile / 8; ++i) {
+        const int kp = kg + 4 * i;
+        uint32_t pw[HW];
+        if constexpr (HW == 4) {
+          const uint4 pp = *reinterpret_cast<const uint4*>(Ps + kp * 16);
+          pw[0] = pp.x;
+          pw[1] = pp.y;
+          pw[2] = pp.z;
+          pw[3] = pp.w;
+        } else {
+#pragma unroll
+          for (int hl = 0; hl < HW; ++hl)
+            pw[hl] = *reinterpret_cast<const uint32_t*>(Ps + (kp * HW + hl) * 4);
+        }
+        const uint4 va =
+            *reinterpret_cast<const uint4*>(Vs + kp * 512 + dg * 32);
+        const uint4 vb =
+            *reinterpret_cast<const uint4*>(Vs + kp * 512 + dg * 32 + 16);
+        const uint32_t vw[8] = {va.x, va.y, va.z, va.w,
+                                vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+        for (int hl = 0; hl < HW; ++hl)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            o[hl][e] = dot2_bf16(pw[hl], vw[e], o[hl][e]);
+      }
+      __syncthreads();
+    }
+
+    // ---- reduce over the 4 key-pair groups and the 64 key lanes, write
+#pragma unroll
+    for (int hl = 0; hl < HW; ++hl) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[hl][e] += __shfl_xor(o[hl][e], 16, 64);
+        o[hl][e] += __shfl_xor(o[hl][e], 32, 64);
+      }
+      lsum[hl] = wave_sum(lsum[hl]);
+    }
+    if (kg == 0) {
+#pragma unroll
+      for (int hl = 0; hl < HW; ++hl) {
+        float* dst = part + 2 * HPW + (w * HW + hl) * kD + dg * 8;
+        if constexpr (FUSED) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) store_dev(dst + e, o[hl][e]);
+        } else {
+          float4* d4 = reinterpret_cast<float4*>(dst);
+          d4[0] = make_float4(o[hl][0], o[hl][1], o[hl][2], o[hl][3]);
+          d4[1] = make_float4(o[hl][4], o[hl][5], o[hl][6], o[hl][7]);
+        }
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int hl = 0; hl < HW; ++hl) {
+        if constexpr (FUSED) {
+          store_dev(part + w * HW + hl, m[hl]);
+          store_dev(part + HPW + w * HW + hl, lsum[hl]);
+        } else {
+          part[w * HW + hl] = m[hl];
+          part[HPW + w * HW + hl] = lsum[hl];
+        }
+      }
+    }
+  } else {
+    // a split past this sequence's keys contributes nothing
+    for (int i = tid; i < PF; i += kDecThreads) {
+      const float x = i < HPW ? -INFINITY : 0.0f;
+      if constexpr (FUSED)
+        store_dev(part + i, x);
+      else
+        part[i] = x;
+    }
+  }
+
+  if constexpr (FUSED) {
+  // ---- the last workgroup of this (sequence, KV head, head group) merges.
+  // The partial went out with device-scope stores; once they have completed
+  // the counter is bumped (device scope), and the workgroup that takes the
+  // last ticket reads every partial with device-scope loads.
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0)
+    s_ticket = __hip_atomic_fetch_add(&p.counters[bg * HG + hg], 1,
+                                      __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != p.splits - 1) return;
+
+  static_assert(HPW * kD / 4 == 128, "fused merge covers 4 heads");
+  const int f = tid & 127;            // float4 of the 4 x 128 outputs
+  const int half = tid >> 7;          // splits s = half, half + 2, ...
+  const int hl = f >> 5, d4 = f & 31;
+  float M = -INFINITY, L = 0.0f;
+  float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  constexpr int kBatch = 16;  // up to 32 splits: every load in one batch
+  for (int s0 = half; s0 < p.splits; s0 += 2 * kBatch) {
+    float ms[kBatch], ls[kBatch];
+    float4 os[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int s = s0 + 2 * i;
+      const float* ps = part_base + (size_t)min(s, p.splits - 1) * PF;
+      const float* po = ps + 2 * HPW + hl * kD + d4 * 4;
+      ms[i] = s < p.splits ? load_dev(ps + hl) : -INFINITY;
+      ls[i] = load_dev(ps + HPW + hl);
+      os[i] = make_float4(load_dev(po), load_dev(po + 1), load_dev(po + 2),
+                          load_dev(po + 3));
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (ms[i] == -INFINITY) continue;
+      const float mn = fmaxf(M, ms[i]);
+      const float a = fast_exp2(M - mn), c = fast_exp2(ms[i] - mn);
+      L = L * a + ls[i] * c;
+      O.x = O.x * a + os[i].x * c;
+      O.y = O.y * a + os[i].y * c;
+      O.z = O.z * a + os[i].z * c;
+      O.w = O.w * a + os[i].w * c;
+      M = mn;
+    }
+  }
+  // combine the two halves through LDS
+  float* red = reinterpret_cast<float*>(smem);
+  if (half == 1) {
+    red[f * 6 + 0] = M;
+    red[f * 6 + 1] = L;
+    red[f * 6 + 2] = O.x;
+    red[f * 6 + 3] = O.y;
+    red[f * 6 + 4] = O.z;
+    red[f * 6 + 5] = O.w;
+  }
+  __syncthreads();
+  if (half == 0) {
+    const float M2 = red[f * 6 + 0];
+    const float mn = fmaxf(M, M2);
+    const float a = M == -INFINITY ? 0.0f : fast_exp2(M - mn);
+    const float c = M2 == -INFINITY ? 0.0f : fast_exp2(M2 - mn);
+    const float Lt = L * a + red[f * 6 + 1] * c;
+    const float inv = 1.0f / Lt;
+    float4 r;
+    r.x = (O.x * a + red[f * 6 + 2] * c) * inv;
+    r.y = (O.y * a + red[f * 6 + 3] * c) * inv;
+    r.z = (O.z * a + red[f * 6 + 4] * c) * inv;
+    r.w = (O.w * a + red[f * 6 + 5] * c) * inv;
+    const int h = g * kGroup + hg * HPW + hl;
+    *reinterpret_cast<float4*>(p.out + ((size_t)b * kHq + h) * kD + d4 * 4) = r;
+    if (tid == 0)  // ready for the next call
+      __hip_atomic_store(&p.counters[bg * HG + hg], 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  }  // FUSED
+}
+
+// Merge the split partials of one (sequence, query head, quarter of the
+// head dimension): with M the largest split maximum,
+// o = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s.  256 threads = 8 float4
+// columns x 32 split lanes, so all loads of a column are in flight at once.
+__global__ __launch_bounds__(256) void decode_merge_kernel(
+    const DecodeParams p, int heads_per_wg) {
+  const int dq = blockIdx.x & 3;
+  const int h = (blockIdx.x >> 2) % kHq;
+  const int b = (blockIdx.x >> 2) / kHq;
+  const int g = h / kGroup, hh = h % kGroup;
+  const int hpw = heads_per_wg, hg = hh / hpw, hl = hh % hpw;
+  const int hgroups = kGroup / hpw;
+  const int pf = hpw * (kD + 2);
+  const float* base =
+      p.part + (size_t)((b * kHkv + g) * hgroups + hg) * p.splits * pf;
+  const int tid = threadIdx.x;
+  const int c4 = tid & 7, sl = tid >> 3;
+  const int d = dq * 32 + c4 * 4;
+  float M = -INFINITY, L = 0.0f;
+  float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  constexpr int kBatch = 4;
+  for (int s0 = sl; s0 < p.splits; s0 += 32 * kBatch) {
+    float ms[kBatch], ls[kBatch];
+    float4 os[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int s = s0 + 32 * i;
+      const float* ps = base + (size_t)min(s, p.splits - 1) * pf;
+      ms[i] = s < p.splits ? ps[hl] : -INFINITY;
+      ls[i] = ps[hpw + hl];
+      os[i] = *reinterpret_cast<const float4*>(ps + 2 * hpw + hl * kD + d);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (ms[i] == -INFINITY) continue;
+      const float mn = fmaxf(M, ms[i]);
+      const float a = fast_exp2(M - mn), c = fast_exp2(ms[i] - mn);
+      L = L * a + ls[i] * c;
+      O.x = O.x * a + os[i].x * c;
+      O.y = O.y * a + os[i].y * c;
+      O.z = O.z * a + os[i].z * c;
+      O.w = O.w * a + os[i].w * c;
+      M = mn;
+    }
+  }
+  __shared__ float red[32][8][6];
+  red[sl][c4][0] = M;
+  red[sl][c4][1] = L;
+  red[sl][c4][2] = O.x;
+  red[sl][c4][3] = O.y;
+  red[sl][c4][4] = O.z;
+  red[sl][c4][5] = O.w;
+  __syncthreads();
+  if (sl == 0) {
+    float Mt = -INFINITY;
+    for (int i = 0; i < 32; ++i) Mt = fmaxf(Mt, red[i][c4][0]);
+    float Lt = 0.0f, x = 0.0f, y = 0.0f, z = 0.0f, ww = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+      if (red[i][c4][0] == -INFINITY) continue;
+      const float c = fast_exp2(red[i][c4][0] - Mt);
+      Lt += red[i][c4][1] * c;
+      x += red[i][c4][2] * c;
+      y += red[i][c4][3] * c;
+      z += red[i][c4][4] * c;
+      ww += red[i][c4][5] * c;
+    }
+    const float inv = 1.0f / Lt;
+    *reinterpret_cast<float4*>(p.out + ((size_t)b * kHq + h) * kD + d) =
+        make_float4(x * inv, y * inv, z * inv, ww * inv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
+                         bool local, int B, hipStream_t s) {
+  const dim3 block(kDecThreads);
+  if (plan.narrow) {
+    const int grid = (p.units + 7) / 8 * 8 * plan.head_groups;
+    if (local)
+      hipLaunchKernelGGL((decode_kernel<true, 1, true>), dim3(grid), block, 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<false, 1, true>), dim3(grid), block,
+                         0, s, p);
+    return hipGetLastError();
+  }
+  if (local)
+    hipLaunchKernelGGL((decode_kernel<true, 4, false>), dim3(p.units), block,
+                       0, s, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<false, 4, false>), dim3(p.units), block,
+                       0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(B * kHq * 4), dim3(256), 0, s,
+                     p, plan.heads_per_wg);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

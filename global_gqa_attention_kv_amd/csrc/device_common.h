@@ -1,0 +1,85 @@
+// device_common.h -- small device helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo*b.lo + a.hi*b.hi + c with bf16 pairs packed in 32-bit words
+// (v_dot2_f32_bf16: products exact in fp32, fp32 accumulation).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+  return __builtin_bit_cast(float, w << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+
+// Two floats -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Interleave the bf16 lanes of two words: (a.lo, b.lo) and (a.hi, b.hi).
+__device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+// sin and cos of 2*pi*r for |r| <= 0.5 (v_sin_f32 / v_cos_f32 take their
+// argument in revolutions).
+__device__ __forceinline__ void sincos_rev(float r, float* s, float* c) {
+  *s = __builtin_amdgcn_sinf(r);
+  *c = __builtin_amdgcn_cosf(r);
+}
+
+// Device-scope (all XCDs) coherent store and load of one word: the store is
+// written through to the coherence point instead of staying dirty in this
+// XCD's L2, and the load does not trust a stale L2 copy.  With these, a
+// workgroup can hand data to a workgroup on another XCD inside one launch
+// with only a store-completion wait before a device-scope counter update,
+// instead of a full L2 write-back fence.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): every vector memory operation of this wave has
+// completed (stores acknowledged at their scope).
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+}  // namespace gqa

@@ -1,0 +1,83 @@
+// internal.h -- definitions shared by the host dispatch and the HIP kernels
+// of libgqa_attn.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gqa_attn.h"
+
+namespace gqa {
+
+constexpr int kHq = GQA_NUM_Q_HEADS;      // 32 query heads
+constexpr int kHkv = GQA_NUM_KV_HEADS;    // 2 KV heads
+constexpr int kGroup = kHq / kHkv;        // 16 query heads per KV head
+constexpr int kD = GQA_HEAD_DIM;          // 128
+constexpr int kW = GQA_WINDOW;            // 2048-slot ring
+constexpr int kMaxBatch = GQA_MAX_BATCH;
+constexpr int kTokenElems = kHkv * kD;    // 256 bf16 per token per cache
+
+// ---------------------------------------------------------------- append
+struct AppendParams {
+  const uint16_t* k_new;   // [B][n][2][128]
+  const uint16_t* v_new;
+  uint16_t* k;             // cache base
+  uint16_t* v;
+  int64_t seq_stride;      // elements
+  int64_t capacity;
+  int32_t n;               // tokens per sequence in k_new
+  int32_t first;           // first token index written (local: max(0, n-2048))
+  int32_t local;
+  int32_t pad_;
+  int64_t pos0[kMaxBatch];
+};
+hipError_t launch_kv_append(const AppendParams& p, int B, int count,
+                            hipStream_t s);
+
+// ---------------------------------------------------------------- decode
+constexpr int kDecTile = 64;               // keys per tile
+constexpr int kDecThreads = 256;           // 4 waves
+
+// Two launch shapes share one kernel template:
+//  * wide: a workgroup serves all 16 query heads of its KV head (4 per wave)
+//    and a long key split; a separate kernel merges the splits.  Used where
+//    the cache is large (global layers).
+//  * narrow: a workgroup serves 4 query heads (1 per wave) and a single
+//    tile; the four head groups of one tile run on the same XCD so three of
+//    them hit L2, and the last workgroup of each (sequence, KV head, head
+//    group) merges the splits in the same launch.  Used for the 2048-key
+//    local windows, where latency rather than bandwidth sets the time.
+struct DecodePlan {
+  bool narrow;
+  int heads_per_wg;     // 16 (wide) or 4 (narrow)
+  int head_groups;      // 16 / heads_per_wg
+  int splits;           // S: key splits per (sequence, KV head)
+  int tiles_per_split;  // tiles of kDecTile keys per split
+};
+DecodePlan plan_decode(int kind, int B, int64_t max_keys);
+size_t decode_ws_bytes(int B, const DecodePlan& plan);
+inline int part_floats(const DecodePlan& pl) { return pl.heads_per_wg * (kD + 2); }
+
+struct DecodeParams {
+  const uint16_t* k;       // cache base (sequence 0, slot 0, head 0)
+  uint16_t* k_mut;         // same cache, written when k_new is given
+  const uint16_t* v;
+  uint16_t* v_mut;
+  const uint16_t* k_new;   // [B][1][2][128] new token, or null
+  const uint16_t* v_new;
+  const uint32_t* q;       // [B][32][64] bf16 pairs
+  float* part;             // partial sums, see decode.hip
+  int32_t* counters;       // [B][2][head_groups], zero between calls
+  float* out;              // [B][32][128]
+  int64_t seq_stride;      // elements
+  float scale_log2;        // softmax scale * log2(e)
+  int32_t splits;
+  int32_t tiles_per_split;
+  int32_t units;           // B * 2 * splits
+  float rope_rev[kD / 2];  // local: theta^(-c/64) / (2 pi), revolutions per position
+  int64_t pos[kMaxBatch];
+};
+hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
+                         bool local, int B, hipStream_t s);
+
+}  // namespace gqa

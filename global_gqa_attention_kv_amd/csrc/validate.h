@@ -1,0 +1,21 @@
+// validate.h -- host-side argument checks of the C ABI (plain C++, no HIP).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gqa_attn.h"
+
+namespace gqa {
+
+// Visible keys of a query at `pos` on a layer of `kind`.
+int64_t visible_keys(int kind, int64_t pos);
+
+int check_layer(const gqa_layer* L);
+int check_append(const gqa_layer* L, const void* k_new, const void* v_new,
+                 const int64_t* pos0, int B, int n);
+// On success *max_keys is the largest visible-key count over the batch.
+int check_decode(const gqa_layer* L, const void* q, const int64_t* pos, int B,
+                 const float* out, int64_t* max_keys);
+
+}  // namespace gqa

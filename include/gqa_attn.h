@@ -1,0 +1,140 @@
+/*
+ * gqa_attn.h -- C ABI of libgqa_attn.so: grouped-query attention with a
+ * hybrid local / global KV cache on AMD MI355X (gfx950).
+ *
+ * The model shape is compiled in: 32 query heads share 2 KV heads of
+ * dimension 128; query head h reads KV head h / 16.  Layers repeat three
+ * local layers and one global layer.
+ *   - Local layer: RoPE (base rope_theta) on queries and keys; each query at
+ *     position i attends to positions max(0, i-2047) .. i.  Its cache is a
+ *     ring of 2048 slots, slot = position mod 2048.
+ *   - Global layer: no RoPE; each query at position i attends to positions
+ *     0 .. i.  Its cache is linear, slot = position, up to 131072 slots.
+ * Sources: "Deep dive into Muse Glimmer" (shishifenxi.com) section 01 (52
+ * layers, 32 query / 2 KV heads, dim 128, 3 local then 1 global, nearby 2048
+ * tokens, about 1024 B of KV per token per layer); "Tomas Koutsky explains
+ * how Meta fits Muse Glimmer into 24 GB" (runtimewire.com), "Narrow cache"
+ * (131,072-token context, sliding-window entries reused cyclically) and "Long
+ * context still costs compute" (global layers omit RoPE).
+ *
+ * Conventions for every entry point
+ *   - All tensors are device pointers, bf16 unless stated, dense row-major,
+ *     16-byte aligned.  Positions are HOST arrays of int64, one per sequence.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  The library never allocates, frees or synchronises, keeps no
+ *     global mutable state and is safe to call from several threads on
+ *     different streams.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     non-zero return means nothing was enqueued (except GQA_ERR_HIP, which
+ *     reports a failed launch).  Faults inside a kernel surface at the
+ *     caller's next synchronisation.  No C++ exception crosses the ABI.
+ *   - Batch size B is 1 .. GQA_MAX_BATCH.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ABI_VERSION 1
+
+#define GQA_NUM_Q_HEADS 32
+#define GQA_NUM_KV_HEADS 2
+#define GQA_HEAD_DIM 128
+#define GQA_WINDOW 2048
+#define GQA_MAX_CONTEXT 131072
+#define GQA_MAX_BATCH 64
+
+/* Layer kinds. */
+#define GQA_LOCAL 0
+#define GQA_GLOBAL 1
+
+/* Operations, for gqa_workspace_bytes. */
+#define GQA_OP_DECODE 0
+
+/* Status codes. */
+#define GQA_OK 0
+#define GQA_ERR_INVALID_ARG (-1)  /* null pointer, B or n out of range      */
+#define GQA_ERR_POS_RANGE (-2)    /* position < 0, or past a global cache   */
+#define GQA_ERR_MISALIGNED (-3)   /* a pointer or stride not 16-B aligned    */
+#define GQA_ERR_WS_TOO_SMALL (-4) /* workspace smaller than required        */
+#define GQA_ERR_UNSUPPORTED (-5)  /* layer descriptor outside compiled shape */
+#define GQA_ERR_HIP (-6)          /* a kernel launch failed                  */
+
+/* One attention layer's cache, owned by the caller.
+ *   kind       GQA_LOCAL or GQA_GLOBAL
+ *   window     GQA_WINDOW for local layers, 0 for global layers
+ *   capacity   slots per sequence: GQA_WINDOW (local) or 1..GQA_MAX_CONTEXT
+ *              (global)
+ *   rope_theta RoPE base for local layers (> 0), 0 for global layers
+ *   k, v       device bf16 caches [B][capacity][2][128]; sequence b starts at
+ *              element b * seq_stride
+ *   seq_stride elements between sequences, >= capacity * 256, multiple of 8 */
+typedef struct gqa_layer {
+  int32_t kind;
+  int32_t window;
+  int64_t capacity;
+  double rope_theta;
+  void* k;
+  void* v;
+  int64_t seq_stride;
+} gqa_layer;
+
+/* Append n tokens per sequence to a layer's cache (bit-exact copy).
+ * k_new, v_new: [B][n][2][128] bf16; token t of sequence b has position
+ * pos0[b] + t.  Global layers write slot = position (pos0[b] + n must not
+ * exceed capacity).  Local layers write slot = position mod 2048 and, when
+ * n > 2048, only the last 2048 tokens (the earlier ones would be overwritten
+ * anyway), so no two writes of one call collide.  n >= 1.
+ * Pages: runtimewire.com "Narrow cache" (cyclic reuse of sliding-window
+ * entries; about 1024 B per token per layer, shishifenxi.com section 01). */
+int gqa_kv_append(const gqa_layer* layer, const void* k_new, const void* v_new,
+                  const int64_t* pos0, int B, int n, void* stream);
+
+/* One decode step: one query token per sequence at position pos[b], whose
+ * own K/V is already in the cache.  q: [B][32][128] bf16; out: [B][32][128]
+ * fp32.  Global layers attend to positions 0..pos[b] (pos[b] < capacity);
+ * local layers to max(0, pos[b]-2047)..pos[b] through the ring, with RoPE.
+ * Scale 1/sqrt(128).  The key range is split across workgroups (split-K)
+ * whose partial softmax sums are merged on the device.
+ * Workspace: `ws` (256-byte aligned) must hold
+ * gqa_workspace_bytes(GQA_OP_DECODE, kind, B, 1, max pos + 1) bytes and be
+ * zero-filled once before its first use; every call leaves it zero-filled
+ * again (it holds split counters), so one workspace serves any number of
+ * calls issued in order on one stream.  Calls that may overlap in time need
+ * separate workspaces.
+ * Pages: shishifenxi.com section 01 (each new token reads the cached keys
+ * and values); runtimewire.com "Narrow cache" and "Long context still costs
+ * compute". */
+int gqa_attn_decode(const gqa_layer* layer, const void* q, const int64_t* pos,
+                    int B, float* out, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* gqa_kv_append(layer, k_new, v_new, pos, B, 1) followed by
+ * gqa_attn_decode(layer, q, pos, ...), in one launch: the new token's K/V
+ * (k_new, v_new: [B][1][2][128] bf16) is stored to its slot and used as the
+ * last key of the attention.  Same workspace rules as gqa_attn_decode. */
+int gqa_attn_decode_append(const gqa_layer* layer, const void* q,
+                           const void* k_new, const void* v_new,
+                           const int64_t* pos, int B, float* out, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Workspace bytes an operation needs for any call on a layer of `kind` with
+ * batch B, n tokens per sequence and context (keys visible to the last
+ * query) at most max_ctx.  Returns 0 for invalid arguments. */
+size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx);
+
+/* A static description of a status code. */
+const char* gqa_status_string(int status);
+
+/* GQA_ABI_VERSION of the loaded library. */
+int gqa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

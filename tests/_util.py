@@ -1,0 +1,62 @@
+"""Shared helpers of the GPU parity tests: cache set-up through the library's
+own append, oracle calls on the same bytes, and the tolerance check."""
+import numpy as np
+import torch
+
+import global_gqa_attention_kv_amd as ga
+import oracle
+import synth_inputs as si
+
+# bf16 inputs, fp32 accumulation, compared with the fp64 oracle
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def sentinel_cache(kind, B, capacity=None, device="cuda"):
+    """A layer whose caches are filled with the 0xFFFF bit pattern."""
+    if capacity is None:
+        capacity = ga.WINDOW if kind == ga.LOCAL else ga.MAX_CONTEXT
+    shape = (B, capacity, ga.HKV, ga.D)
+    k = torch.full(shape, -1, dtype=torch.int16, device=device).view(torch.bfloat16)
+    v = torch.full(shape, -1, dtype=torch.int16, device=device).view(torch.bfloat16)
+    return ga.Layer(kind, k, v)
+
+
+def fill_layer(layer, streams, positions):
+    """Append each sequence's logical stream up to and including its query
+    position: global layers get positions 0..p, local layers the last 2048
+    of them.  streams[b] = (k [n,2,128], v) on the CPU, row r = position r."""
+    for b, (k, v) in enumerate(streams):
+        p = positions[b]
+        lo = 0 if layer.kind == ga.GLOBAL else max(0, p - ga.WINDOW + 1)
+        kk = k[lo:p + 1].unsqueeze(0).contiguous().cuda()
+        vv = v[lo:p + 1].unsqueeze(0).contiguous().cuda()
+        sub = ga.Layer(layer.kind, layer.k[b:b + 1], layer.v[b:b + 1],
+                       layer.rope_theta)
+        ga.kv_append(sub, kk, vv, [lo])
+
+
+def oracle_decode(kind, q_cpu, streams, positions):
+    """fp64 oracle for one decode query per sequence."""
+    outs = []
+    for b, (k, v) in enumerate(streams):
+        p = positions[b]
+        lo = 0 if kind == ga.GLOBAL else max(0, p - ga.WINDOW + 1)
+        outs.append(oracle.attend(
+            si.bits(q_cpu[b:b + 1]), [p], si.bits(k[lo:p + 1]),
+            si.bits(v[lo:p + 1]), lo, hq=ga.HQ, hkv=ga.HKV, d=ga.D,
+            window=ga.WINDOW if kind == ga.LOCAL else 0,
+            rope=kind == ga.LOCAL, theta=10000.0)[0])
+    return np.stack(outs)
+
+
+def check_close(got, want, what, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - want)
+    rms = float(np.sqrt(np.mean(want ** 2))) or 1.0
+    msg = "%s: max abs %.3e, mean abs %.3e, max/rms %.3e" % (
+        what, err.max(), err.mean(), err.max() / rms)
+    print(msg, flush=True)
+    assert np.isfinite(got).all(), what + ": non-finite output"
+    assert err.max() <= max_abs and err.mean() <= mean_abs, msg
+    return err

@@ -1,0 +1,177 @@
+"""Host-only checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function include/gqa_attn.h declares,
+agree with the header's constants, and reject bad arguments with the
+documented status codes before it touches the GPU.  Device pointers here are
+fake addresses: validation never dereferences them, and every call below
+fails validation, so no HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import global_gqa_attention_kv_amd as ga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f)
+           for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
+
+
+def _header_text():
+    return "\n".join(open(h).read() for h in HEADERS)
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_\w+)\s*\(", text)))
+
+
+def _defines():
+    out = {}
+    for name, val in re.findall(r"#define\s+(GQA_\w+)\s+\(?(-?\d+)\)?",
+                                _header_text()):
+        out[name] = int(val)
+    return out
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ga.library_path()):
+        pytest.fail("libgqa_attn.so is not built (run __graft_entry__.build())")
+    return ga._load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert "gqa_attn_decode" in names and "gqa_kv_append" in names
+    for n in names:
+        assert hasattr(lib, n), "missing export %s" % n
+
+
+def test_constants_match_header(lib):
+    D = _defines()
+    assert lib.gqa_abi_version() == D["GQA_ABI_VERSION"]
+    assert (ga.HQ, ga.HKV, ga.D, ga.WINDOW, ga.MAX_CONTEXT, ga.MAX_BATCH) == (
+        D["GQA_NUM_Q_HEADS"], D["GQA_NUM_KV_HEADS"], D["GQA_HEAD_DIM"],
+        D["GQA_WINDOW"], D["GQA_MAX_CONTEXT"], D["GQA_MAX_BATCH"])
+    assert (ga.LOCAL, ga.GLOBAL) == (D["GQA_LOCAL"], D["GQA_GLOBAL"])
+    for code in ("GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_POS_RANGE",
+                 "GQA_ERR_MISALIGNED", "GQA_ERR_WS_TOO_SMALL",
+                 "GQA_ERR_UNSUPPORTED", "GQA_ERR_HIP"):
+        s = ga.status_string(D[code])
+        assert s and s != "unknown status"
+    assert ga.status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    for kind in (ga.LOCAL, ga.GLOBAL):
+        prev = 0
+        for ctx in (1, 63, 64, 65, 2048, 4096, 32768, 131072):
+            n = ga.workspace_bytes(ga.OP_DECODE, kind, 1, 1, ctx)
+            assert n > 0 and n % 16 == 0 and n >= prev
+            prev = n
+        assert ga.workspace_bytes(ga.OP_DECODE, kind, 4, 1, 131072) >= prev
+    assert ga.workspace_bytes(ga.OP_DECODE, ga.GLOBAL, 1, 1, 131073) == 0
+    assert ga.workspace_bytes(ga.OP_DECODE, ga.GLOBAL, 0, 1, 10) == 0
+    assert ga.workspace_bytes(ga.OP_DECODE, ga.GLOBAL, 65, 1, 10) == 0
+    assert ga.workspace_bytes(ga.OP_DECODE, 7, 1, 1, 10) == 0
+    assert ga.workspace_bytes(99, ga.GLOBAL, 1, 1, 10) == 0
+    # local layers never see more than the window
+    assert (ga.workspace_bytes(ga.OP_DECODE, ga.LOCAL, 1, 1, 131072) ==
+            ga.workspace_bytes(ga.OP_DECODE, ga.LOCAL, 1, 1, 2048))
+
+
+FAKE = 0x7f0000000000  # 16-byte aligned, never dereferenced
+
+
+def _layer(kind=ga.GLOBAL, capacity=4096, window=None, theta=None, k=FAKE,
+           v=FAKE + (1 << 30), stride=None):
+    if window is None:
+        window = ga.WINDOW if kind == ga.LOCAL else 0
+    if theta is None:
+        theta = 10000.0 if kind == ga.LOCAL else 0.0
+    if kind == ga.LOCAL and capacity == 4096:
+        capacity = ga.WINDOW
+    if stride is None:
+        stride = capacity * 256
+    return ga._CLayer(kind, window, capacity, theta, k, v, stride)
+
+
+def _pos(*vals):
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+D_ = _defines()
+E_ARG, E_POS, E_ALN = (D_["GQA_ERR_INVALID_ARG"], D_["GQA_ERR_POS_RANGE"],
+                       D_["GQA_ERR_MISALIGNED"])
+E_WS, E_UNS = D_["GQA_ERR_WS_TOO_SMALL"], D_["GQA_ERR_UNSUPPORTED"]
+
+
+def _append(lib, L, B=1, n=1, k=FAKE, v=FAKE, pos=None):
+    pos = pos if pos is not None else _pos(*([0] * B))
+    return lib.gqa_kv_append(ctypes.byref(L) if L is not None else None, k, v,
+                             pos, B, n, None)
+
+
+def test_append_validation(lib):
+    L = _layer()
+    assert _append(lib, None) == E_ARG
+    assert _append(lib, L, k=None) == E_ARG
+    assert _append(lib, L, B=0) == E_ARG
+    assert _append(lib, L, B=65, pos=_pos(*([0] * 65))) == E_ARG
+    assert _append(lib, L, n=0) == E_ARG
+    assert _append(lib, _layer(k=0)) == E_ARG
+    assert _append(lib, _layer(kind=5)) == E_UNS
+    assert _append(lib, _layer(kind=ga.LOCAL, capacity=4096 * 2)) == E_UNS
+    assert _append(lib, _layer(kind=ga.LOCAL, theta=0.0)) == E_UNS
+    assert _append(lib, _layer(kind=ga.LOCAL, window=1024)) == E_UNS
+    assert _append(lib, _layer(theta=10000.0)) == E_UNS     # global with RoPE
+    assert _append(lib, _layer(capacity=131073)) == E_UNS
+    assert _append(lib, _layer(stride=100)) == E_ARG
+    assert _append(lib, _layer(stride=4096 * 256 + 4)) == E_ALN
+    assert _append(lib, _layer(k=FAKE + 8)) == E_ALN
+    assert _append(lib, L, k=FAKE + 2) == E_ALN
+    assert _append(lib, L, pos=_pos(-1)) == E_POS
+    assert _append(lib, L, n=2, pos=_pos(4095)) == E_POS        # past capacity
+    assert _append(lib, L, B=2, n=1, pos=_pos(0, 4096)) == E_POS
+
+
+def _decode(lib, L, B=1, q=FAKE, out=FAKE, pos=None, ws=FAKE, ws_bytes=1 << 30):
+    pos = pos if pos is not None else _pos(*([0] * B))
+    return lib.gqa_attn_decode(ctypes.byref(L) if L is not None else None, q,
+                               pos, B, out, ws, ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    L = _layer()
+    assert _decode(lib, None) == E_ARG
+    assert _decode(lib, L, q=None) == E_ARG
+    assert _decode(lib, L, out=None) == E_ARG
+    assert _decode(lib, L, B=0) == E_ARG
+    assert _decode(lib, L, ws=None) == E_ARG
+    assert _decode(lib, _layer(kind=3)) == E_UNS
+    assert _decode(lib, L, q=FAKE + 4) == E_ALN
+    assert _decode(lib, L, out=FAKE + 4) == E_ALN
+    assert _decode(lib, L, ws=FAKE + 8) == E_ALN
+    assert _decode(lib, L, pos=_pos(4096)) == E_POS              # pos < capacity
+    assert _decode(lib, L, pos=_pos(-3)) == E_POS
+    assert _decode(lib, _layer(kind=ga.LOCAL), pos=_pos(1 << 40)) == E_POS
+    need = ga.workspace_bytes(ga.OP_DECODE, ga.GLOBAL, 1, 1, 4096)
+    assert _decode(lib, L, pos=_pos(4095), ws_bytes=need - 1) == E_WS
+    assert _decode(lib, L, pos=_pos(4095), ws_bytes=0) == E_WS
+
+
+def test_decode_append_validation(lib):
+    L = _layer()
+    pos = _pos(10)
+
+    def call(kn=FAKE, vn=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return lib.gqa_attn_decode_append(ctypes.byref(L), FAKE, kn, vn, pos, 1,
+                                          FAKE, ws, ws_bytes, None)
+    assert call(kn=None) == E_ARG
+    assert call(vn=None) == E_ARG
+    assert call(kn=FAKE + 2) == E_ALN
+    assert call(ws=FAKE + 16) == E_ALN     # workspace needs 256-byte alignment
+    assert call(ws_bytes=8) == E_WS
