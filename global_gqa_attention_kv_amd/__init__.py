@@ -18,7 +18,8 @@ import os
 import torch
 
 __all__ = [
-    "LOCAL", "GLOBAL", "OP_DECODE", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
+    "LOCAL", "GLOBAL", "OP_DECODE", "OP_VERIFY", "OP_PREFILL", "MAX_VERIFY",
+    "attn_verify", "attn_prefill", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
     "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
     "attn_decode", "attn_decode_append", "workspace_bytes", "workspace", "status_string", "abi_version",
     "library_path", "layer_kind",
@@ -28,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libgqa_attn.so")
 
 LOCAL, GLOBAL = 0, 1
-OP_DECODE = 0
+OP_DECODE, OP_VERIFY, OP_PREFILL = 0, 1, 2
+MAX_VERIFY = 16
 HQ, HKV, D, WINDOW, MAX_CONTEXT, MAX_BATCH = 32, 2, 128, 2048, 131072, 64
 ROPE_THETA = 10000.0
 
@@ -76,6 +78,12 @@ def _load():
         lib.gqa_kv_append.argtypes = [L, p, p, p, i32, i32, p]
         lib.gqa_attn_decode.restype = i32
         lib.gqa_attn_decode.argtypes = [L, p, p, i32, p, p, ctypes.c_size_t, p]
+        lib.gqa_attn_verify.restype = i32
+        lib.gqa_attn_verify.argtypes = [L, p, p, p, p, i32, i32, p, p,
+                                        ctypes.c_size_t, p]
+        lib.gqa_attn_prefill.restype = i32
+        lib.gqa_attn_prefill.argtypes = [L, p, p, p, p, i32, i32, p, p,
+                                         ctypes.c_size_t, p]
         lib.gqa_attn_decode_append.restype = i32
         lib.gqa_attn_decode_append.argtypes = [L, p, p, p, p, i32, p, p,
                                                ctypes.c_size_t, p]
@@ -230,3 +238,48 @@ def attn_decode_append(layer: Layer, q, k_new, v_new, pos, out=None, ws=None,
     return _decode_common(_load().gqa_attn_decode_append,
                           "gqa_attn_decode_append", layer, q, pos, out, ws,
                           stream, extra=(kp, vp))
+
+
+def _block_common(fn, name, op, out_dtype, layer, q, k_blk, v_blk, pos0, out,
+                  ws, stream):
+    B, n = int(q.shape[0]), int(q.shape[1])
+    qp = _dev(q, torch.bfloat16, (B, n, HQ, D), "q")
+    kp = _dev(k_blk, torch.bfloat16, (B, n, HKV, D), "k_blk")
+    vp = _dev(v_blk, torch.bfloat16, (B, n, HKV, D), "v_blk")
+    if out is None:
+        out = torch.empty((B, n, HQ, D), dtype=out_dtype, device=q.device)
+    op_ = _dev(out, out_dtype, (B, n, HQ, D), "out")
+    posc = _positions(pos0, B)
+    if ws is None:
+        need = workspace_bytes(op, layer.kind, B, n,
+                               max(int(x) for x in posc) + n)
+        if need == 0:
+            raise GqaError(-1, name)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp = _dev(ws, ws.dtype, None, "ws")
+    rc = fn(layer.c_ref, qp, kp, vp, posc, B, n, op_, wp,
+            ws.numel() * ws.element_size(), _stream(stream))
+    if rc != 0:
+        raise GqaError(rc, name)
+    return out
+
+
+def attn_verify(layer: Layer, q, k_blk, v_blk, pos0, out=None, ws=None,
+                stream=None):
+    """Verify a drafted block: q bf16 [B, n, 32, 128] (n <= 16) at positions
+    pos0[b] .. pos0[b]+n-1; k_blk, v_blk bf16 [B, n, 2, 128] (not yet in the
+    cache).  Returns fp32 [B, n, 32, 128].  The cache is not modified."""
+    return _block_common(_load().gqa_attn_verify, "gqa_attn_verify",
+                         OP_VERIFY, torch.float32, layer, q, k_blk, v_blk,
+                         pos0, out, ws, stream)
+
+
+def attn_prefill(layer: Layer, q, k_chunk, v_chunk, pos0, out=None, ws=None,
+                 stream=None):
+    """Prefill a chunk: q bf16 [B, n, 32, 128] at positions pos0[b] ..
+    pos0[b]+n-1 with its own K/V (k_chunk, v_chunk bf16 [B, n, 2, 128], not
+    yet in the cache).  Returns bf16 [B, n, 32, 128].  The cache is not
+    modified; append the chunk with :func:`kv_append` afterwards."""
+    return _block_common(_load().gqa_attn_prefill, "gqa_attn_prefill",
+                         OP_PREFILL, torch.bfloat16, layer, q, k_chunk,
+                         v_chunk, pos0, out, ws, stream)

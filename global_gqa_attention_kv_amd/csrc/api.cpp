@@ -52,6 +52,44 @@ size_t decode_ws_bytes(int B, const DecodePlan& plan) {
   return align256(parts) + align256((size_t)B * kHkv * plan.head_groups * 4);
 }
 
+// Block operations.  Verification (<= 16 tokens) uses 16-token workgroups
+// and splits the key range so about kBlockTargetWGs workgroups run; prefill
+// uses 8-token workgroups and splits keys only when the query groups alone
+// cannot fill the device.
+namespace {
+constexpr int kBlockTargetWGs = 256;
+}
+
+BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify) {
+  BlockPlan p;
+  p.qpw = verify ? 16 : 8;
+  p.qgroups = (n + p.qpw - 1) / p.qpw;
+  // keys one workgroup may see: its window (local) or everything before it
+  const int64_t wg_keys =
+      kind == GQA_LOCAL ? (int64_t)kW - 1 + p.qpw : max_keys;
+  const int64_t tiles = (wg_keys + kBlkTile - 1) / kBlkTile;
+  const int64_t groups = (int64_t)p.qgroups * kHkv * B;
+  int64_t splits = 1;
+  if (groups < kBlockTargetWGs)
+    splits = (kBlockTargetWGs + groups - 1) / groups;
+  if (splits > tiles) splits = tiles;
+  if (splits < 1) splits = 1;
+  p.splits = (int)splits;
+  p.klin_bytes = kind == GQA_LOCAL
+                     ? align256((size_t)B * ((size_t)kW + n) * kTokenElems * 2)
+                     : 0;
+  p.part_bytes = p.splits > 1
+                     ? align256((size_t)B * kHkv * p.qgroups * p.splits *
+                                p.qpw * kGroup * 132 * sizeof(float))
+                     : 0;
+  return p;
+}
+
+size_t block_ws_bytes(const BlockPlan& plan) {
+  const size_t n = plan.klin_bytes + plan.part_bytes;
+  return n ? n : 256;
+}
+
 }  // namespace gqa
 
 using namespace gqa;
@@ -81,6 +119,13 @@ size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx) {
     case GQA_OP_DECODE: {
       const int64_t keys = visible_keys(kind, max_ctx - 1);
       return decode_ws_bytes(B, plan_decode(kind, B, keys));
+    }
+    case GQA_OP_VERIFY:
+    case GQA_OP_PREFILL: {
+      const bool verify = op == GQA_OP_VERIFY;
+      if (n > (verify ? GQA_MAX_VERIFY : GQA_MAX_CONTEXT)) return 0;
+      const int64_t keys = visible_keys(kind, max_ctx - 1);
+      return block_ws_bytes(plan_block(kind, B, n, keys, verify));
     }
     default:
       return 0;
@@ -172,6 +217,62 @@ int gqa_attn_decode_append(const gqa_layer* layer, const void* q,
   if (!k_new || !v_new) return GQA_ERR_INVALID_ARG;
   return decode_impl(layer, q, k_new, v_new, pos, B, out, ws, ws_bytes,
                      stream);
+}
+
+static int block_impl(const gqa_layer* layer, const void* q,
+                      const void* k_blk, const void* v_blk,
+                      const int64_t* pos0, int B, int n, void* out, void* ws,
+                      size_t ws_bytes, bool verify, void* stream) {
+  int64_t max_keys = 0;
+  int rc = check_block(layer, q, k_blk, v_blk, pos0, B, n, out, verify,
+                       &max_keys);
+  if (rc != GQA_OK) return rc;
+  const BlockPlan plan = plan_block(layer->kind, B, n, max_keys, verify);
+  if (!ws) return GQA_ERR_INVALID_ARG;
+  if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
+  if (ws_bytes < block_ws_bytes(plan)) return GQA_ERR_WS_TOO_SMALL;
+  BlockParams p;
+  memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_blk = static_cast<const uint16_t*>(k_blk);
+  p.v_blk = static_cast<const uint16_t*>(v_blk);
+  p.k_cache = static_cast<const uint16_t*>(layer->k);
+  p.v_cache = static_cast<const uint16_t*>(layer->v);
+  p.k_lin = plan.klin_bytes ? static_cast<uint16_t*>(ws) : nullptr;
+  p.part = plan.part_bytes ? reinterpret_cast<float*>(
+                                 static_cast<char*>(ws) + plan.klin_bytes)
+                           : nullptr;
+  p.out = out;
+  p.seq_stride = layer->seq_stride;
+  p.klin_rows = (int64_t)kW + n;
+  p.n = n;
+  p.qgroups = plan.qgroups;
+  p.splits = plan.splits;
+  p.scale_log2 = (float)(1.0 / sqrt((double)kD) * 1.4426950408889634);
+  const bool local = layer->kind == GQA_LOCAL;
+  if (local) {
+    for (int c = 0; c < kD / 2; ++c)
+      p.rope_rev[c] = (float)(pow(layer->rope_theta, -(double)c / (kD / 2)) /
+                              (2.0 * 3.14159265358979323846));
+  }
+  for (int b = 0; b < B; ++b) p.pos0[b] = pos0[b];
+  hipError_t e = launch_block(p, plan, local, verify, B, (hipStream_t)stream);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_attn_verify(const gqa_layer* layer, const void* q, const void* k_blk,
+                    const void* v_blk, const int64_t* pos0, int B, int n,
+                    float* out, void* ws, size_t ws_bytes, void* stream) {
+  return block_impl(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
+                    true, stream);
+}
+
+int gqa_attn_prefill(const gqa_layer* layer, const void* q,
+                     const void* k_chunk, const void* v_chunk,
+                     const int64_t* pos0, int B, int n, void* out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return block_impl(layer, q, k_chunk, v_chunk, pos0, B, n, out, ws,
+                    ws_bytes, false, stream);
 }
 
 }  // extern "C"

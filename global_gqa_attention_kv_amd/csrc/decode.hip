@@ -58,26 +58,6 @@ __device__ __forceinline__ int64_t slot_of(int64_t position, bool local) {
   return local ? (position & (kW - 1)) : position;
 }
 
-// Rotate the 8 dims (d, d+64) held in lo/hi by `delta` positions.
-__device__ __forceinline__ void rope_rotate(uint4& lo, uint4& hi, float delta,
-                                            const float* rev) {
-  uint32_t* l = reinterpret_cast<uint32_t*>(&lo);
-  uint32_t* h = reinterpret_cast<uint32_t*>(&hi);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float x0 = bf16_lo(l[e]), x1 = bf16_hi(l[e]);
-    const float y0 = bf16_lo(h[e]), y1 = bf16_hi(h[e]);
-    float r0 = delta * rev[2 * e], r1 = delta * rev[2 * e + 1];
-    r0 -= rintf(r0);
-    r1 -= rintf(r1);
-    float s0, c0, s1, c1;
-    sincos_rev(r0, &s0, &c0);
-    sincos_rev(r1, &s1, &c1);
-    l[e] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
-    h[e] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
-  }
-}
-
 template <bool LOCAL, int HW, bool FUSED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const DecodeParams p) {

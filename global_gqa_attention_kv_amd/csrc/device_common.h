@@ -71,6 +71,34 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// RoPE on bf16 data: rotate the pairs (lo[i], hi[i]) -- dims d and d + 64
+// of one head -- by `delta` positions, where rev[i] is the pair's frequency
+// in revolutions per position.  The angle is reduced to [-1/2, 1/2]
+// revolution before the hardware sine/cosine; results are rounded to bf16.
+__device__ __forceinline__ void rope_pair(uint32_t& lo, uint32_t& hi,
+                                          float delta, float f0, float f1) {
+  const float x0 = bf16_lo(lo), x1 = bf16_hi(lo);
+  const float y0 = bf16_lo(hi), y1 = bf16_hi(hi);
+  float r0 = delta * f0, r1 = delta * f1;
+  r0 -= rintf(r0);
+  r1 -= rintf(r1);
+  float s0, c0, s1, c1;
+  sincos_rev(r0, &s0, &c0);
+  sincos_rev(r1, &s1, &c1);
+  lo = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+  hi = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+}
+
+// Rotate the 8 dims held in lo (dims d..d+7) against their partners in hi
+// (dims d+64..d+71); rev points at the 8 frequencies of dims d..d+7.
+__device__ __forceinline__ void rope_rotate(uint4& lo, uint4& hi, float delta,
+                                            const float* rev) {
+  rope_pair(lo.x, hi.x, delta, rev[0], rev[1]);
+  rope_pair(lo.y, hi.y, delta, rev[2], rev[3]);
+  rope_pair(lo.z, hi.z, delta, rev[4], rev[5]);
+  rope_pair(lo.w, hi.w, delta, rev[6], rev[7]);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));

@@ -80,4 +80,44 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
                          bool local, int B, hipStream_t s);
 
+// ---------------------------------------------------------------- block
+// A block of n query tokens per sequence at positions pos0 .. pos0+n-1 whose
+// K/V (k_blk, v_blk) are not in the cache yet: chunked prefill (n up to a
+// few thousand, bf16 output) and speculative verification (n <= 16, fp32
+// output, keys split across workgroups).
+constexpr int kBlkTile = 64;               // keys per tile
+constexpr int kMaxPrefill = GQA_MAX_CONTEXT;
+
+struct BlockPlan {
+  int qpw;          // query tokens per workgroup (x 16 heads = rows)
+  int qgroups;      // ceil(n / qpw)
+  int splits;       // key splits (1 = no partials)
+  size_t klin_bytes;   // local: pre-rotated keys
+  size_t part_bytes;   // split partials
+};
+BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify);
+size_t block_ws_bytes(const BlockPlan& plan);
+
+struct BlockParams {
+  const uint16_t* q;        // [B][n][32][128]
+  const uint16_t* k_blk;    // [B][n][2][128]
+  const uint16_t* v_blk;
+  const uint16_t* k_cache;  // layer cache base
+  const uint16_t* v_cache;
+  uint16_t* k_lin;          // local: rotated keys [B][klin_rows][2][128]
+  float* part;              // split partials
+  void* out;                // [B][n][32][128], bf16 or fp32
+  int64_t seq_stride;       // cache elements per sequence
+  int64_t klin_rows;        // rows of k_lin per sequence
+  int32_t n;
+  int32_t qgroups;
+  int32_t splits;
+  int32_t pad_;
+  float scale_log2;
+  float rope_rev[kD / 2];
+  int64_t pos0[kMaxBatch];
+};
+hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
+                        bool local, bool out_f32, int B, hipStream_t s);
+
 }  // namespace gqa

@@ -73,4 +73,27 @@ int check_decode(const gqa_layer* L, const void* q, const int64_t* pos, int B,
   return GQA_OK;
 }
 
+int check_block(const gqa_layer* L, const void* q, const void* k_blk,
+                const void* v_blk, const int64_t* pos0, int B, int n,
+                const void* out, bool verify, int64_t* max_keys) {
+  if (!q || !k_blk || !v_blk || !pos0 || !out || B < 1 || B > GQA_MAX_BATCH ||
+      n < 1 || n > (verify ? GQA_MAX_VERIFY : GQA_MAX_CONTEXT))
+    return GQA_ERR_INVALID_ARG;
+  int rc = check_layer(L);
+  if (rc != GQA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) ||
+      !aligned16(out))
+    return GQA_ERR_MISALIGNED;
+  int64_t mk = 0;
+  for (int b = 0; b < B; ++b) {
+    if (pos0[b] < 0 || pos0[b] + n - 1 > kMaxPos) return GQA_ERR_POS_RANGE;
+    if (L->kind == GQA_GLOBAL && pos0[b] + n > L->capacity)
+      return GQA_ERR_POS_RANGE;
+    const int64_t k = visible_keys(L->kind, pos0[b] + n - 1);
+    if (k > mk) mk = k;
+  }
+  *max_keys = mk;
+  return GQA_OK;
+}
+
 }  // namespace gqa

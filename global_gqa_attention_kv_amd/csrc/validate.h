@@ -18,4 +18,10 @@ int check_append(const gqa_layer* L, const void* k_new, const void* v_new,
 int check_decode(const gqa_layer* L, const void* q, const int64_t* pos, int B,
                  const float* out, int64_t* max_keys);
 
+// Verification (verify = true, n <= 16) or prefill of a block of n tokens.
+// On success *max_keys is the largest key count any query of the call sees.
+int check_block(const gqa_layer* L, const void* q, const void* k_blk,
+                const void* v_blk, const int64_t* pos0, int B, int n,
+                const void* out, bool verify, int64_t* max_keys);
+
 }  // namespace gqa

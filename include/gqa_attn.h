@@ -48,6 +48,7 @@ extern "C" {
 #define GQA_WINDOW 2048
 #define GQA_MAX_CONTEXT 131072
 #define GQA_MAX_BATCH 64
+#define GQA_MAX_VERIFY 16
 
 /* Layer kinds. */
 #define GQA_LOCAL 0
@@ -55,6 +56,8 @@ extern "C" {
 
 /* Operations, for gqa_workspace_bytes. */
 #define GQA_OP_DECODE 0
+#define GQA_OP_VERIFY 1
+#define GQA_OP_PREFILL 2
 
 /* Status codes. */
 #define GQA_OK 0
@@ -122,6 +125,41 @@ int gqa_attn_decode_append(const gqa_layer* layer, const void* q,
                            const void* k_new, const void* v_new,
                            const int64_t* pos, int B, float* out, void* ws,
                            size_t ws_bytes, void* stream);
+
+/* Speculative verification of a drafted block of n (1..GQA_MAX_VERIFY)
+ * tokens per sequence at positions pos0[b] .. pos0[b]+n-1, in one pass.
+ * q: [B][n][32][128] bf16; k_blk, v_blk: [B][n][2][128] bf16, the block's
+ * own K/V, NOT yet in the cache (the cache holds every position < pos0[b]);
+ * out: [B][n][32][128] fp32.  Token r attends to the cached positions before
+ * pos0[b] in its range (global: all of them; local: those >= pos0[b]+r-2047,
+ * through the ring, with RoPE) and to block tokens 0..r (causal inside the
+ * block).  The call does not touch the cache: append the accepted prefix
+ * afterwards with gqa_kv_append, so rejected drafts never overwrite ring
+ * entries that are still inside the window.  Global layers need
+ * pos0[b] + n <= capacity.  ws (256-byte aligned, no initialisation) must
+ * hold gqa_workspace_bytes(GQA_OP_VERIFY, kind, B, n, max pos0 + n) bytes.
+ * Pages: shishifenxi.com section 04 (a block of 16 drafted tokens verified
+ * by the main model at once); kongchang.com "Meta open-sources the 30B Muse
+ * Glimmer", "Trick 3: D-Flash" (parallel verification under the causal
+ * mask). */
+int gqa_attn_verify(const gqa_layer* layer, const void* q, const void* k_blk,
+                    const void* v_blk, const int64_t* pos0, int B, int n,
+                    float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Chunked prefill: n (1..GQA_MAX_CONTEXT) prompt tokens per sequence at
+ * positions pos0[b] .. pos0[b]+n-1.  Same visibility rules and arguments as
+ * gqa_attn_verify (the chunk's K/V are passed in and not appended; the
+ * cache holds the positions before pos0[b]), but out is bf16 [B][n][32][128],
+ * rounded to nearest even from fp32.  ws (256-byte aligned, no
+ * initialisation) must hold gqa_workspace_bytes(GQA_OP_PREFILL, kind, B, n,
+ * max pos0 + n) bytes.  Append the chunk with gqa_kv_append afterwards.
+ * Pages: runtimewire.com "Long context still costs compute" (global layers
+ * run full attention during prompt processing with memory-efficient kernels
+ * that never store the attention matrix; the cost stays quadratic). */
+int gqa_attn_prefill(const gqa_layer* layer, const void* q,
+                     const void* k_chunk, const void* v_chunk,
+                     const int64_t* pos0, int B, int n, void* out, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* Workspace bytes an operation needs for any call on a layer of `kind` with
  * batch B, n tokens per sequence and context (keys visible to the last

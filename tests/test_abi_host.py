@@ -175,3 +175,38 @@ def test_decode_append_validation(lib):
     assert call(kn=FAKE + 2) == E_ALN
     assert call(ws=FAKE + 16) == E_ALN     # workspace needs 256-byte alignment
     assert call(ws_bytes=8) == E_WS
+
+
+@pytest.mark.parametrize("fn", ["gqa_attn_verify", "gqa_attn_prefill"])
+def test_block_validation(lib, fn):
+    f = getattr(lib, fn)
+    L = _layer()
+
+    def call(layer=L, q=FAKE, kb=FAKE, vb=FAKE, pos=None, B=1, n=16, out=FAKE,
+             ws=FAKE, ws_bytes=1 << 30):
+        pos = pos if pos is not None else _pos(*([0] * B))
+        return f(ctypes.byref(layer) if layer is not None else None, q, kb, vb,
+                 pos, B, n, out, ws, ws_bytes, None)
+    assert call(layer=None) == E_ARG
+    assert call(q=None) == E_ARG
+    assert call(kb=None) == E_ARG
+    assert call(out=None) == E_ARG
+    assert call(n=0) == E_ARG
+    assert call(B=0) == E_ARG
+    assert call(ws=None) == E_ARG
+    if fn == "gqa_attn_verify":
+        assert call(n=17) == E_ARG                      # block of at most 16
+    else:
+        assert call(n=17, pos=_pos(0), ws_bytes=0) == E_WS
+    assert call(layer=_layer(kind=9)) == E_UNS
+    assert call(vb=FAKE + 4) == E_ALN
+    assert call(ws=FAKE + 64) == E_ALN
+    assert call(pos=_pos(4096 - 15)) == E_POS           # pos0 + n > capacity
+    assert call(pos=_pos(-1)) == E_POS
+    need = ga.workspace_bytes(ga.OP_VERIFY if fn == "gqa_attn_verify"
+                              else ga.OP_PREFILL, ga.GLOBAL, 1, 16, 4096)
+    assert need > 0
+    assert call(pos=_pos(4080), ws_bytes=need - 1) == E_WS
+    # local layers need room for the rotated window in the workspace
+    loc = ga.workspace_bytes(ga.OP_PREFILL, ga.LOCAL, 1, 4096, 131072)
+    assert loc >= (2048 + 4096) * 512

@@ -1,0 +1,183 @@
+"""Verify (drafted block, n <= 16) and chunked prefill on the GPU against
+the fp64 oracle.
+
+Tolerance: max abs <= 2e-2, mean abs <= 2e-3.  Beyond random inputs: the
+cache must be left untouched by both calls, verify row r must agree with a
+decode at pos0 + r once block tokens 0..r are appended (the two entry points
+compute the same function), a zero query must give the exact window mean,
+and the full-size shapes (verify at 131056 + 16, prefill's last 4096-token
+chunk of 131072) are checked on sampled rows plus the edge rows."""
+import numpy as np
+import pytest
+import torch
+
+import global_gqa_attention_kv_amd as ga
+import oracle
+import synth_inputs as si
+from tests._util import check_close, fill_layer, oracle_decode, sentinel_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_rows(kind, q_cpu, streams, pos0, rows):
+    """fp64 oracle for block tokens `rows` of each sequence."""
+    out = []
+    for b, (k, v) in enumerate(streams):
+        qpos = [pos0[b] + r for r in rows]
+        lo = 0 if kind == ga.GLOBAL else max(0, min(qpos) - ga.WINDOW + 1)
+        hi = max(qpos) + 1
+        out.append(oracle.attend(
+            si.bits(q_cpu[b, rows]), qpos, si.bits(k[lo:hi]), si.bits(v[lo:hi]),
+            lo, hq=ga.HQ, hkv=ga.HKV, d=ga.D,
+            window=ga.WINDOW if kind == ga.LOCAL else 0,
+            rope=kind == ga.LOCAL, theta=10000.0))
+    return np.stack(out)
+
+
+def _setup(kind, pos0, n, seed, capacity=None):
+    """Caches holding every position before pos0[b]; returns the layer,
+    the logical streams (positions 0 .. pos0+n-1), the block tensors."""
+    B = len(pos0)
+    streams = [si.stream(si.seq_seed(seed, b), pos0[b] + n) for b in range(B)]
+    if kind == ga.GLOBAL and capacity is None:
+        capacity = max(pos0) + n
+    layer = sentinel_cache(kind, B, capacity)
+    for b in range(B):
+        if pos0[b] > 0:
+            sub = ga.Layer(kind, layer.k[b:b + 1], layer.v[b:b + 1])
+            lo = 0 if kind == ga.GLOBAL else max(0, pos0[b] - ga.WINDOW)
+            ga.kv_append(sub, streams[b][0][None, lo:pos0[b]].contiguous().cuda(),
+                         streams[b][1][None, lo:pos0[b]].contiguous().cuda(), [lo])
+    kb = torch.stack([streams[b][0][pos0[b]:pos0[b] + n] for b in range(B)])
+    vb = torch.stack([streams[b][1][pos0[b]:pos0[b] + n] for b in range(B)])
+    q = torch.stack([si.queries(si.seq_seed(seed, b) + 555, n) for b in range(B)])
+    return layer, streams, q, kb, vb
+
+
+def _snapshot(layer):
+    return (layer.k.view(torch.int16).clone(), layer.v.view(torch.int16).clone())
+
+
+def _unchanged(layer, snap):
+    return (torch.equal(layer.k.view(torch.int16), snap[0]) and
+            torch.equal(layer.v.view(torch.int16), snap[1]))
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+@pytest.mark.parametrize("n", [1, 5, 16])
+def test_verify_ragged(kind, n):
+    pos0 = [0, 63, 2047, 2048, 5000]
+    print("verify kind=%d n=%d pos0=%s" % (kind, n, pos0), flush=True)
+    layer, streams, q, kb, vb = _setup(kind, pos0, n, seed=2001 + n)
+    snap = _snapshot(layer)
+    out = ga.attn_verify(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    assert _unchanged(layer, snap), "verify must not write the cache"
+    want = _oracle_rows(kind, q, streams, pos0, list(range(n)))
+    check_close(out.cpu().numpy(), want, "verify kind=%d n=%d" % (kind, n))
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_verify_full_size_131056(kind):
+    # 16 drafted tokens at 131056..131071 over a 131056-token prior context
+    pos0 = [131056]
+    cap = ga.MAX_CONTEXT if kind == ga.GLOBAL else None
+    print("verify full kind=%d" % kind, flush=True)
+    layer, streams, q, kb, vb = _setup(kind, pos0, 16, seed=1004, capacity=cap)
+    out = ga.attn_verify(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    want = _oracle_rows(kind, q, streams, pos0, list(range(16)))
+    check_close(out.cpu().numpy(), want, "verify 131056+16 kind=%d" % kind)
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_verify_rows_equal_decode_after_append(kind):
+    """Verify token r == decode at pos0 + r once tokens 0..r are appended."""
+    pos0, n = [3000, 9000], 16
+    layer, streams, q, kb, vb = _setup(kind, pos0, n, seed=2010,
+                                       capacity=20000 if kind == ga.GLOBAL
+                                       else None)
+    ver = ga.attn_verify(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    ver = ver.cpu().numpy()
+    ws = ga.workspace(ga.OP_DECODE, kind, 2, 1, 20000)
+    for r in range(n):
+        pos = [p + r for p in pos0]
+        dec = ga.attn_decode_append(layer, q[:, r].contiguous().cuda(),
+                                    kb[:, r:r + 1].contiguous().cuda(),
+                                    vb[:, r:r + 1].contiguous().cuda(), pos,
+                                    ws=ws)
+        torch.cuda.synchronize()
+        err = np.abs(dec.cpu().numpy() - ver[:, r]).max()
+        assert err < 1e-2, "row %d differs by %.3e" % (r, err)
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+@pytest.mark.parametrize("pos0,n", [([0], 300), ([0, 4096], 257), ([4096], 4096),
+                                    ([2000], 100), ([1], 8)])
+def test_prefill_small(kind, pos0, n):
+    print("prefill kind=%d pos0=%s n=%d" % (kind, pos0, n), flush=True)
+    layer, streams, q, kb, vb = _setup(kind, pos0, n, seed=3001 + n)
+    snap = _snapshot(layer)
+    out = ga.attn_prefill(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    assert _unchanged(layer, snap), "prefill must not write the cache"
+    rows = sorted(set(list(range(min(n, 40))) + list(range(max(0, n - 40), n)) +
+                      [int(x) for x in np.random.default_rng(n).integers(0, n, 64)]))
+    want = _oracle_rows(kind, q, streams, pos0, rows)
+    got = out.float().cpu().numpy()[:, rows]
+    check_close(got, want, "prefill kind=%d pos0=%s n=%d" % (kind, pos0, n))
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_prefill_zero_query_window_mean(kind):
+    pos0, n = [5000], 64
+    layer, streams, q, kb, vb = _setup(kind, pos0, n, seed=3100)
+    q = torch.zeros_like(q)
+    out = ga.attn_prefill(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    v = streams[0][1].double().numpy()
+    got = out.float().cpu().numpy()[0]
+    for r in (0, 1, 31, 63):
+        i = pos0[0] + r
+        lo = 0 if kind == ga.GLOBAL else i - ga.WINDOW + 1
+        mean = np.repeat(v[lo:i + 1].mean(axis=0), 16, axis=0)
+        err = np.abs(got[r] - mean).max()
+        assert err < 4e-3, "row %d: %.3e (bf16 output)" % (r, err)
+
+
+def test_prefill_then_append_chunks_match_single_chunk():
+    """Two chunks (prefill + append, prefill) reproduce one big chunk."""
+    kind, n = ga.GLOBAL, 1024
+    layer, streams, q, kb, vb = _setup(kind, [0], 2 * n, seed=3200)
+    whole = ga.attn_prefill(layer, q.cuda(), kb.cuda(), vb.cuda(), [0])
+    first = ga.attn_prefill(layer, q[:, :n].contiguous().cuda(),
+                            kb[:, :n].contiguous().cuda(),
+                            vb[:, :n].contiguous().cuda(), [0])
+    ga.kv_append(layer, kb[:, :n].contiguous().cuda(),
+                 vb[:, :n].contiguous().cuda(), [0])
+    second = ga.attn_prefill(layer, q[:, n:].contiguous().cuda(),
+                             kb[:, n:].contiguous().cuda(),
+                             vb[:, n:].contiguous().cuda(), [n])
+    torch.cuda.synchronize()
+    both = torch.cat([first, second], dim=1)
+    diff = (both.float() - whole.float()).abs().max().item()
+    assert diff <= 1e-2, diff
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_prefill_last_chunk_131072_sampled(kind):
+    """The last 4096-token chunk of a 131072-token prompt (the quadratic
+    worst case), checked on 48 random rows plus the first and last rows."""
+    pos0, n = [131072 - 4096], 4096
+    cap = ga.MAX_CONTEXT if kind == ga.GLOBAL else None
+    print("prefill last chunk kind=%d" % kind, flush=True)
+    layer, streams, q, kb, vb = _setup(kind, pos0, n, seed=1005, capacity=cap)
+    out = ga.attn_prefill(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 1, 7, 8, 63, 64, 2047, 2048, n - 2, n - 1] +
+                      [int(x) for x in rng.integers(0, n, 48)]))
+    want = _oracle_rows(kind, q, streams, pos0, rows)
+    got = out.float().cpu().numpy()[:, rows]
+    check_close(got, want, "prefill last chunk kind=%d" % kind)
