@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 N_LAYERS = 52
 CTX = 131072
 
@@ -138,6 +139,103 @@ def time_global_decode(ga, torch, layers, qs, outs, ws, positions, kinds,
     return e0.elapsed_time(e1) / n
 
 
+def pairs_block(kind, pos0, n, window=2048):
+    """Unmasked (query, key) pairs of a block of n tokens at pos0."""
+    total = 0
+    for r in range(n):
+        i = pos0 + r
+        total += i + 1 if kind == 1 else min(i + 1, window)
+    return total
+
+
+def bench_verify(ga, torch, layers, kinds, B, reps=5, seed=4004):
+    """52-layer verification of a 16-token drafted block at 131056..131071
+    over the caches of the decode step (their first 131056 positions serve as
+    the prior context).  Returns a dict of figures."""
+    dev = torch.device("cuda")
+    n, pos0 = 16, CTX - 16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    blk = []
+    for l in range(N_LAYERS):
+        q = torch.randn((B, n, ga.HQ, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        kb = torch.randn((B, n, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        vb = torch.randn((B, n, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        blk.append((q, kb, vb))
+    ws = torch.empty(max(ga.workspace_bytes(ga.OP_VERIFY, k, B, n, CTX)
+                         for k in (ga.LOCAL, ga.GLOBAL)), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, n, ga.HQ, ga.D), dtype=torch.float32, device=dev)
+    positions = [pos0] * B
+
+    def step():
+        for l in range(N_LAYERS):
+            q, kb, vb = blk[l]
+            ga.attn_verify(layers[l], q, kb, vb, positions, out, ws)
+
+    ms, _ = time_graph(torch, step, reps, 2)
+    flops = 0
+    kvb = 0
+    for kind in kinds:
+        pr = pairs_block(kind, pos0, n)
+        flops += B * pr * 4 * ga.HQ * ga.D
+        keys = CTX if kind == ga.GLOBAL else min(CTX, 2048 + n - 1)
+        kvb += B * keys * 1024
+    return {"ms_per_step": round(ms, 4),
+            "kv_GBps": round(kvb / (ms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(kvb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "workload": "52-layer verify, 16 drafted tokens at 131056..131071, "
+                        "batch %d" % B}
+
+
+def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005):
+    """Chunked causal prefill of `total` tokens in `chunk`-token chunks on
+    one local and one global layer: prefill then append per chunk."""
+    dev = torch.device("cuda")
+    res = {}
+    for kind in (ga.LOCAL, ga.GLOBAL):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed + kind)
+        layer = ga.Layer.allocate(kind, 1, device=dev)
+        q = torch.randn((1, total, ga.HQ, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((1, total, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((1, total, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        ws = torch.empty(ga.workspace_bytes(ga.OP_PREFILL, kind, 1, chunk, total),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty((1, chunk, ga.HQ, ga.D), dtype=torch.bfloat16, device=dev)
+
+        def run():
+            for c0 in range(0, total, chunk):
+                sl = slice(c0, c0 + chunk)
+                ga.attn_prefill(layer, q[:, sl], k[:, sl], v[:, sl], [c0], out, ws)
+                ga.kv_append(layer, k[:, sl], v[:, sl], [c0])
+
+        run()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = pairs_block(kind, 0, total) * 4 * ga.HQ * ga.D
+        name = "local" if kind == ga.LOCAL else "global"
+        res[name] = {"ms": round(ms, 3),
+                     "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
+                                        MFMA_PEAK_TFLOPS, 4),
+                     "algorithmic_flop": flops}
+        del q, k, v, layer, ws, out
+        torch.cuda.empty_cache()
+    res["workload"] = ("prefill of %d tokens in %d-token chunks (prefill + "
+                       "append per chunk), batch 1" % (total, chunk))
+    return res
+
+
 def cpu_baseline(ga, torch, layers, qs, positions, kinds, budget_s=20.0):
     """The fp64 oracle on this host: one decode step for sequence 0 over as
     many layers (in step order) as fit the time budget."""
@@ -192,6 +290,8 @@ def main():
     ap.add_argument("--batch", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="decode step only (skip verify and prefill)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the attention path has no "
@@ -259,6 +359,13 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(ga, torch, layers, qs, positions,
                                             kinds)
+    if not args.no_extras:
+        line["verify"] = bench_verify(ga, torch, layers, kinds, 1)
+        print("# verify done", file=sys.stderr, flush=True)
+        del layers, qs, outs, ws, step
+        torch.cuda.empty_cache()
+        line["prefill"] = bench_prefill(ga, torch)
+        print("# prefill done", file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
 

@@ -57,16 +57,6 @@ constexpr int kKsB = kBlkTile * kKRow;      // 17408
 constexpr int kVtB = kD * kVRow;            // 17408
 constexpr int kPartRow = 132;               // floats: o[128], m, l, pad
 
-// Calls f(I) for I = 0 .. N-1 with I a compile-time constant, so register
-// arrays indexed by I stay in registers.
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 __device__ __forceinline__ uint32_t word(const uint4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }

@@ -50,6 +50,7 @@ namespace gqa {
 
 namespace {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kTau = 8.0f;  // lazy-rescale threshold in log2 units
 constexpr int kKsBytes = kDecTile * 256;        // 64 rows x 256 B
 constexpr int kVsBytes = (kDecTile / 2) * 512;  // 32 key pairs x 128 words
@@ -126,12 +127,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const uint16_t* Kn = p.k_new + (int64_t)b * kTokenElems + g * kD;
     const uint16_t* Vn = p.v_new + (int64_t)b * kTokenElems + g * kD;
     const int head0 = g * kGroup + hg * HPW + w * HW;  // this wave's heads
-    // The query never changes during the kernel: reading it through the
-    // constant address space lets the compiler use scalar loads (SGPR
-    // operands) for these wave-uniform words.
-    const __attribute__((address_space(4))) uint32_t* qw =
-        (const __attribute__((address_space(4))) uint32_t*)(
-            p.q + ((int64_t)b * kHq + head0) * (kD / 2));
+    // The wave's HW query rows (64 bf16 pairs each) held as wave-uniform
+    // words for the DPP broadcast: within every 16-lane row, lane n keeps
+    // pairs (n % LPH) * PPL .. + PPL - 1 of head n / LPH in qv[0 .. PPL).
+    constexpr int LPH = 16 / HW;       // lanes per head
+    constexpr int PPL = 4 * HW;        // pairs per lane = VGPRs used
+    uint32_t qv[PPL];
+    {
+      const int n = lane & 15;
+      const uint32_t* src = p.q +
+                            ((int64_t)b * kHq + head0 + n / LPH) * (kD / 2) +
+                            (n % LPH) * PPL;
+#pragma unroll
+      for (int v = 0; v < PPL; v += 4) {
+        const uint4 w4 = *reinterpret_cast<const uint4*>(src + v);
+        qv[v] = w4.x;
+        qv[v + 1] = w4.y;
+        qv[v + 2] = w4.z;
+        qv[v + 3] = w4.w;
+      }
+    }
 
     uint4 kreg[2][2];  // [unit][dims 8c..8c+7 | 8c+64..8c+71]
     uint4 vreg[2][2];  // [unit][key 2r | key 2r+1]
@@ -217,31 +232,56 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
       __syncthreads();
       if (t + 1 < ntiles) load_tile(t + 1);
 
-      // ---- scores: lane = key of this tile, HW heads per wave
-      float acc[HW];
+      // ---- scores: lane = key of this tile, HW heads per wave; the query
+      // word of (head hl, pair p) is broadcast from lane hl*LPH + p/PPL.
+      // The lane's K row is read from LDS in 4 batches of 64 B, one batch
+      // ahead of the products; consecutive products alternate between
+      // heads so no product waits on the previous one's accumulator.
+      // A DPP instruction must not read (in any operand) a VGPR written by
+      // either of the two VALU instructions before it: every head keeps
+      // NACC partial sums, so consecutive products always update different
+      // accumulators, four instructions apart.
+      constexpr int NACC = 4 / HW;
+      float acc[HW][NACC];
 #pragma unroll
-      for (int hl = 0; hl < HW; ++hl) acc[hl] = 0.0f;
+      for (int hl = 0; hl < HW; ++hl)
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[hl][a] = 0.0f;
       const uint8_t* krow = Ks + lane * 256;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const uint4 kc =
-            *reinterpret_cast<const uint4*>(krow + ((c ^ (lane & 15)) << 4));
-#pragma unroll
-        for (int hl = 0; hl < HW; ++hl) {
-          const __attribute__((address_space(4))) uint32_t* qr =
-              qw + hl * (kD / 2) + c * 4;
-          acc[hl] = dot2_bf16(qr[0], kc.x, acc[hl]);
-          acc[hl] = dot2_bf16(qr[1], kc.y, acc[hl]);
-          acc[hl] = dot2_bf16(qr[2], kc.z, acc[hl]);
-          acc[hl] = dot2_bf16(qr[3], kc.w, acc[hl]);
-        }
-      }
+      u32x4_t kbuf[2][4];
+      auto read_batch = [&](auto Bt, u32x4_t(&dst)[4]) {
+        static_for<0, 4>([&](auto J) {
+          constexpr int C = 4 * Bt + J;
+          dst[J] = *reinterpret_cast<const u32x4_t*>(
+              krow + ((C ^ (lane & 15)) << 4));
+        });
+      };
+      read_batch(std::integral_constant<int, 0>{}, kbuf[0]);
+      static_for<0, 4>([&](auto Bt) {
+        if constexpr (Bt + 1 < 4)
+          read_batch(std::integral_constant<int, Bt + 1>{},
+                     kbuf[(Bt + 1) & 1]);
+        static_for<0, 4>([&](auto J) {
+          constexpr int C = 4 * Bt + J;
+          static_for<0, 4>([&](auto I) {
+            constexpr int pr = 4 * C + I;
+            static_for<0, HW>([&](auto HL) {
+              constexpr int ii = I, bb = Bt & 1, jj = J, hh = HL;
+              acc[hh][ii % NACC] = dot2_bf16_bcast<HL * LPH + pr / PPL>(
+                  qv[pr % PPL], kbuf[bb][jj][ii], acc[hh][ii % NACC]);
+            });
+          });
+        });
+      });
       const bool valid = k_begin + t * kDecTile + lane < k_end;
       float s2[HW];
       bool need = false;
 #pragma unroll
       for (int hl = 0; hl < HW; ++hl) {
-        s2[hl] = valid ? acc[hl] * p.scale_log2 : -INFINITY;
+        float a = acc[hl][0];
+#pragma unroll
+        for (int k = 1; k < NACC; ++k) a += acc[hl][k];
+        s2[hl] = valid ? a * p.scale_log2 : -INFINITY;
         need |= s2[hl] > m[hl] + kTau;
       }
       if (__any(need)) {  // wave-uniform: raise the running maximum

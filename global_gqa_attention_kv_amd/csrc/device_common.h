@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gqa {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -14,6 +16,32 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c,
                                          false);
+}
+
+// acc += dot2(word broadcast from lane LANE of this lane's 16-lane row of q,
+// k).  The DPP row_newbcast operand lets 16 distinct wave-uniform words live
+// in one VGPR (replicated in the four rows) instead of SGPRs.  Hazard: none
+// of q, k, acc may have been written by either of the two VALU instructions
+// before this one (the compiler cannot see that the asm is a DPP op); the
+// callers interleave independent accumulators, and a host test checks the
+// generated code.
+template <int LANE>
+__device__ __forceinline__ float dot2_bf16_bcast(uint32_t q, uint32_t k,
+                                                 float acc) {
+  asm("v_dot2c_f32_bf16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf "
+      "bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(q), "v"(k), "i"(LANE));
+  return acc;
+}
+
+// Calls f(I) for I = 0 .. N-1 with I a compile-time constant.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) {
