@@ -40,6 +40,26 @@ def _ensure_built():
     return ga
 
 
+def measured_traffic(B):
+    """HBM bytes per launch of the global-layer decode kernel from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by a plain copy
+    (profiles/decode_global_131072_b4_hbm_counters.md).  None when the
+    counters were taken on other kernel sources or another batch size."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "decode_global_traffic.json")) as f:
+            rec = json.load(f)
+        csrc = os.path.join(ROOT, "global_gqa_attention_kv_amd", "csrc")
+        h = hashlib.sha256(b"".join(
+            open(os.path.join(csrc, n), "rb").read()
+            for n in ("decode.hip", "device_common.h", "internal.h"))).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if h != rec.get("source_sha256") or B != 4:
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
 def kv_bytes_step(kinds, positions):
     """Algorithmic KV bytes of one decode step: each layer reads every
     visible key's K and V for both KV heads (1024 B per token)."""
@@ -292,6 +312,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-extras", action="store_true",
                     help="decode step only (skip verify and prefill)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB, "
+                         "to scale hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the attention path has no "
@@ -302,6 +325,14 @@ def main():
     import torch
     ga = _ensure_built()
     torch.cuda.set_device(0)
+    if args.calibrate_copy_mib:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads and writes exactly nbytes each
+        torch.cuda.synchronize()
+        del src, dst
     B = args.batch
     pos = CTX - 1
     kinds, layers, qs, outs, ws, positions, step = build_decode_step(
@@ -351,7 +382,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(B),
+            "traffic_unit": "bytes per launch (HBM fetched + written)",
             "avg_ms": round(kms, 5),
             "algorithmic_bytes": kbytes,
         },
