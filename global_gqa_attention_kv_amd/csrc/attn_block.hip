@@ -26,8 +26,9 @@
 //    key order inside each 16-key step follows the score layout; V^T is read
 //    in that same order.
 //  * K tiles sit in LDS row-major (rows padded to 272 B); V tiles are
-//    transposed on their way into LDS (rows of 64 keys padded to 136 B) so a
-//    lane reads 4 consecutive keys of one dimension with one 8-byte load.
+//    transposed on their way into LDS (rows of 64 keys padded to 136 B, the
+//    8-byte units XOR-swizzled by dim/8 against write conflicts) so a lane
+//    reads 4 consecutive keys of one dimension with one 8-byte load.
 //  * Online softmax in the log2 domain with a lazy maximum (rescale only when
 //    a score exceeds the running maximum by more than 2^8); masks are applied
 //    only on tiles that cross the causal diagonal or the window edge.
@@ -201,10 +202,16 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
       const int key = u >> 4, c = u & 15;
       *reinterpret_cast<u32x4_t*>(Ks + key * kKRow + c * 16) = kreg[I];
     });
+    // V^T rows are stored with the 8-byte (4-key) units XOR-swizzled by
+    // (dim / 8): without it the 16 lanes of a write group, which hold dims
+    // 8c + e for c = 0..15, would hit only 4 bank groups.
     const int kq = tid >> 4, c = tid & 15;
     static_for<0, 4>([&](auto E) {
       // dims 8c+2e and 8c+2e+1 of keys KPU*kq .. KPU*kq+KPU-1
-      uint8_t* even = Vt + (8 * c + 2 * E) * kVRow + 2 * KPU * kq;
+      const int unit = (KPU * kq) >> 2;          // 8-byte unit of the keys
+      const int sub = (KPU * kq) & 3;            // key offset inside it
+      uint8_t* even =
+          Vt + (8 * c + 2 * E) * kVRow + ((unit ^ c) << 3) + 2 * sub;
       uint8_t* odd = even + kVRow;
       if constexpr (KPU == 4) {
         const uint32_t w0 = word(vreg[0], E), w1 = word(vreg[1], E);
@@ -249,27 +256,31 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
       }
     }
 
-    // ---- softmax update for this lane's row
+    // ---- softmax update for this lane's row.  The maximum is taken on raw
+    // scores (the scale is positive) and the scale is folded into the
+    // exponent: p = 2^(s * scale_log2 - m).
     const int kb = k_lo + (t_begin + t) * kBlkTile;
     const bool edge = (kb + kBlkTile - 1 > i_first) ||
                       (LOCAL && kb <= i_last - kW);
-    // key kb + off + 4 hi5 is visible iff off <= rel and (local) off > rel - W
-    const int rel = qpos - kb - 4 * hi5;
+    if (edge) {
+      // key kb + off + 4 hi5 is visible iff off <= rel and (local)
+      // off > rel - W
+      const int rel = qpos - kb - 4 * hi5;
+#pragma unroll
+      for (int be = 0; be < 2; ++be)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int off = 32 * be + 8 * (i >> 2) + (i & 3);
+          const bool ok = off <= rel && (!LOCAL || off > rel - kW);
+          S[be][i] = ok ? S[be][i] : -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int be = 0; be < 2; ++be)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = S[be][i] * p.scale_log2;
-        if (edge) {
-          const int off = 32 * be + 8 * (i >> 2) + (i & 3);
-          const bool ok = off <= rel && (!LOCAL || off > rel - kW);
-          s = ok ? s : -INFINITY;
-        }
-        S[be][i] = s;
-        mt = fmaxf(mt, s);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, S[be][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.scale_log2;
     if (__any(mt > m_run + kTauB)) {
       const float mn = fmaxf(m_run, mt);
       const float alpha = mn == m_run ? 1.0f : fast_exp2(m_run - mn);
@@ -280,29 +291,41 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
     }
+    // a row that has seen no visible key yet keeps m = -inf; any finite
+    // base then turns its -inf scores into zero weights
+    const float mb = m_run == -INFINITY ? 0.0f : m_run;
     bf16x8_t P[4];  // 16-key contraction steps: (block be, half tt)
 #pragma unroll
     for (int be = 0; be < 2; ++be)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt) {
+        uint32_t w4[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float s = S[be][8 * tt + j];
-          const float pv = s == -INFINITY ? 0.0f : fast_exp2(s - m_run);
-          const __bf16 pb = (__bf16)pv;
-          l_run += (float)pb;  // the denominator sums the weights P.V uses
-          P[2 * be + tt][j] = pb;
+        for (int j = 0; j < 4; ++j) {
+          const float p0 =
+              fast_exp2(fmaf(S[be][8 * tt + 2 * j], p.scale_log2, -mb));
+          const float p1 =
+              fast_exp2(fmaf(S[be][8 * tt + 2 * j + 1], p.scale_log2, -mb));
+          w4[j] = pack_bf16(p0, p1);
+          // the denominator sums exactly the bf16 weights P.V uses
+          l_run = dot2_bf16(w4[j], 0x3F803F80u, l_run);
         }
+        P[2 * be + tt] = __builtin_bit_cast(
+            bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+      }
 
     // ---- O^T += V^T P^T over four 16-key steps, four 32-dim blocks
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int key0 = 16 * c + 4 * hi5;  // keys key0..+3 and key0+8..+11
+      // keys 16c + 4 hi5 + 0..3 and + 8..11: 8-byte units u0 and u0 + 2
+      const int u0 = 4 * c + hi5;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint8_t* vr = Vt + (32 * d + row) * kVRow + 2 * key0;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+        const int dim = 32 * d + row, sw = dim >> 3;
+        const uint8_t* vr = Vt + dim * kVRow;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr + ((u0 ^ sw) << 3));
+        const uint2 hi =
+            *reinterpret_cast<const uint2*>(vr + (((u0 + 2) ^ sw) << 3));
         const uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
         O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, a4), P[c], O[d], 0, 0, 0);
