@@ -13,7 +13,10 @@ namespace {
 // Wide decode launches aim for about this many workgroups so every compute
 // unit holds a few resident workgroups; each workgroup then streams several
 // tiles.
-constexpr int kDecodeTargetWGs = 768;
+// Global-layer decode: two wide-kernel workgroups fit a CU (66 KB of LDS
+// each), so 512 workgroups on 256 CUs run as one full round (a partial
+// second round would leave half the device idle at the end).
+constexpr int kDecodeTargetWGs = 512;
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
@@ -34,7 +37,7 @@ DecodePlan plan_decode(int kind, int B, int64_t max_keys) {
   p.narrow = false;
   p.heads_per_wg = kGroup;
   p.head_groups = 1;
-  int64_t want = (kDecodeTargetWGs + 2 * B - 1) / (2 * B);
+  int64_t want = kDecodeTargetWGs / (2 * B);
   if (want < 1) want = 1;
   int64_t per = (tiles + want - 1) / want;
   if (per < 1) per = 1;

@@ -464,6 +464,337 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   }  // FUSED
 }
 
+// ---------------------------------------------------------------------------
+// Wide shape (global layers): a workgroup serves all 16 query heads of its KV
+// head (4 per wave) over a long key split; two workgroups share a CU.  The
+// tiles go straight from HBM into a two-slot LDS ring with direct-to-LDS
+// loads (global_load_lds_dwordx4: the 16 bytes of lane l land at the wave's
+// LDS base + 16 l, never passing through VGPRs), marked non-temporal since
+// the cache is streamed once per step; tile t + 1 is in flight while tile t
+// is consumed.
+//  * K rows keep the narrow shape's layout: 16-byte chunk c of key row r sits
+//    at chunk slot c ^ (r & 15) (the lane that fills slot s fetches chunk
+//    s ^ (r & 15)), so lane = key reads its whole row conflict-free.
+//  * V rows stay in key order with chunk c at slot c ^ 2(r & 3).  The P.V
+//    operands are read with ds_read_b64_tr_b16, which gives each lane four
+//    consecutive keys of one dimension: two key-interleaved bf16 pairs, the
+//    operand v_dot2_f32_bf16 wants, with no VALU re-packing.  The XOR puts
+//    the four keys read by each 16-lane group on different banks.
+//  * P.V lanes: lane 16 g + j owns dimensions j, j + 16, ..., j + 112 of its
+//    wave's 4 heads and keys 16 q + 4 g .. + 3 of each 16-key quarter q; the
+//    four groups g are summed at the end.
+//  * The tile loop is unrolled twice so every LDS address is a per-lane
+//    register plus a constant.
+constexpr int kTileBytes = kDecTile * 256;    // one 64-key tile of K or V
+constexpr int kSlotBytes = 2 * kTileBytes;    // K tile, then V tile
+constexpr int kWideHW = 4;                    // query heads per wave
+constexpr int kWidePs = (kDecTile / 2) * kWideHW * 4;  // P bytes per wave
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Direct-to-LDS load of 16 bytes per lane from a per-lane address: lane l's
+// bytes land at LDS byte address lds + 16 l (lds wave-uniform).  Written as
+// inline assembly so the compiler does not hold every later LDS read behind
+// it: the caller waits for completion (s_waitcnt vmcnt) and publishes the
+// data with a barrier.  M0 carries the LDS address; it is saved and
+// restored, and one wait state separates its write from the load.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+// The same from a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16(const uint16_t* base, uint32_t off,
+                                      uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+
+__global__ __launch_bounds__(kDecThreads, 2) void decode_wide_kernel(
+    const DecodeParams p) {
+  constexpr int HW = kWideHW;
+  constexpr int LPH = 16 / HW;       // lanes per head in the q broadcast rows
+  constexpr int PPL = 4 * HW;        // q pairs per lane
+  constexpr int PF = kGroup * (kD + 2);
+  __shared__ __attribute__((aligned(16)))
+  uint8_t smem[2 * kSlotBytes + 4 * kWidePs];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint8_t* Ps = smem + 2 * kSlotBytes + w * kWidePs;
+
+  const int unit = blockIdx.x;
+  if (unit >= p.units) return;
+  const int split = unit % p.splits;
+  const int bg = unit / p.splits;  // b * 2 + g
+  const int g = bg % kHkv;
+  const int b = bg / kHkv;
+
+  const int64_t pos = p.pos[b];
+  const int nkeys = (int)(pos + 1);
+  const int span = p.tiles_per_split * kDecTile;
+  const int k_begin = split * span;
+  const int k_end = min(nkeys, k_begin + span);
+  const bool has_keys = k_begin < nkeys;
+  const int new_key = nkeys - 1;
+  const bool use_new = p.k_new != nullptr;
+  float* const part = p.part + ((size_t)bg * p.splits + split) * PF;
+
+  // the call appends the query's own token (see decode_kernel)
+  if (use_new && g == 0 && has_keys && new_key / span == split && tid < 64) {
+    const bool is_v = tid >= 32;
+    const int chunk = tid & 31;
+    const uint16_t* src = (is_v ? p.v_new : p.k_new) +
+                          (int64_t)b * kTokenElems + chunk * 8;
+    uint16_t* dst = (is_v ? p.v_mut : p.k_mut) + (int64_t)b * p.seq_stride +
+                    pos * kTokenElems + chunk * 8;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+
+  if (!has_keys) {
+    for (int i = tid; i < PF; i += kDecThreads)
+      part[i] = i < kGroup ? -INFINITY : 0.0f;
+    return;
+  }
+
+  const int ntiles = (k_end - k_begin + kDecTile - 1) / kDecTile;
+  const uint16_t* Kb = p.k + (int64_t)b * p.seq_stride + g * kD;
+  const uint16_t* Vb = p.v + (int64_t)b * p.seq_stride + g * kD;
+  const uint16_t* Kn = p.k_new + (int64_t)b * kTokenElems + g * kD;
+  const uint16_t* Vn = p.v_new + (int64_t)b * kTokenElems + g * kD;
+  const int head0 = g * kGroup + w * HW;
+
+  // q words for the DPP broadcast, as in decode_kernel
+  uint32_t qv[PPL];
+  {
+    const int n = lane & 15;
+    const uint32_t* src = p.q +
+                          ((int64_t)b * kHq + head0 + n / LPH) * (kD / 2) +
+                          (n % LPH) * PPL;
+#pragma unroll
+    for (int v = 0; v < PPL; v += 4) {
+      const uint4 w4 = *reinterpret_cast<const uint4*>(src + v);
+      qv[v] = w4.x;
+      qv[v + 1] = w4.y;
+      qv[v + 2] = w4.z;
+      qv[v + 3] = w4.w;
+    }
+  }
+  // The waits in the tile loop count only the tile loads, so the q loads
+  // complete here.  Passing q through an (empty) asm also tells the
+  // compiler the loads are done: it cannot see the waits inside asm and
+  // would otherwise repeat a full vmcnt wait before every use in the loop.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int v = 0; v < PPL; ++v) asm volatile("" : "+v"(qv[v]));
+
+  // Tile t -> slot t % 2.  Wave w fills rows 16w .. 16w+15 of the K and V
+  // tiles, four rows (1 KB) per load: lane l takes row 16w + 4i + l/16 and
+  // chunk slot l % 16.
+  const int rsub = lane >> 4, cs = lane & 15;
+  uint32_t kdma[4], vdma[4];  // byte offsets from the tile's first key
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + rsub;  // == row & 15
+    const uint32_t row = 16 * w + r;
+    kdma[i] = row * (kTokenElems * 2) + ((cs ^ r) << 4);
+    vdma[i] = row * (kTokenElems * 2) + ((cs ^ (2 * (r & 3))) << 4);
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+  auto issue_tile = [&](int t, auto SLOT) {
+    const int kb = k_begin + t * kDecTile;
+    const uint32_t kl = __builtin_amdgcn_readfirstlane(
+        lds_base + SLOT * kSlotBytes + w * 16 * 256);
+    if (kb + kDecTile <= k_end && (!use_new || new_key >= kb + kDecTile)) {
+      // a full tile of cached keys
+      const uint16_t* kt = Kb + (int64_t)kb * kTokenElems;
+      const uint16_t* vt = Vb + (int64_t)kb * kTokenElems;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dma16(kt, kdma[i], kl + i * 1024);
+        dma16(vt, vdma[i], kl + kTileBytes + i * 1024);
+      }
+    } else {
+      // the split's last tile: keys past its end repeat the last key (they
+      // are masked), and the query's own key comes from k_new / v_new
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + rsub;
+        const int key = min(kb + 16 * w + r, k_end - 1);
+        const bool fresh = use_new && key == new_key;
+        const uint16_t* krow = fresh ? Kn : Kb + (int64_t)key * kTokenElems;
+        const uint16_t* vrow = fresh ? Vn : Vb + (int64_t)key * kTokenElems;
+        dma16(krow + ((cs ^ r) << 3), kl + i * 1024);
+        dma16(vrow + ((cs ^ (2 * (r & 3))) << 3), kl + kTileBytes + i * 1024);
+      }
+    }
+  };
+
+  float m[HW], lsum[HW], o[HW][8];
+#pragma unroll
+  for (int hl = 0; hl < HW; ++hl) {
+    m[hl] = -INFINITY;
+    lsum[hl] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hl][e] = 0.0f;
+  }
+
+  // LDS read offsets: the K row of key = lane, and the P.V transposes (the
+  // 16-lane group kg reads keys 16q + 4kg + (j >> 2), dims 16e + 4(j & 3)).
+  const int kg = lane >> 4, jl = lane & 15, ja = jl & 3, je = jl >> 2;
+  uint32_t krd[16], vrd[8];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) krd[c] = lds_base + lane * 256 + ((c ^ jl) << 4);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    vrd[e] = lds_base + kTileBytes + (4 * kg + je) * 256 + 32 * (e ^ je) + 8 * ja;
+  const uint32_t prd = (uint32_t)(uintptr_t)Ps + 32 * kg;
+
+  auto consume = [&](int t, auto SLOT) {
+    constexpr uint32_t so = SLOT * kSlotBytes;
+    // ---- scores (lane = key), exactly as in decode_kernel
+    constexpr int NACC = 4 / HW;
+    float acc[HW][NACC];
+#pragma unroll
+    for (int hl = 0; hl < HW; ++hl)
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) acc[hl][a] = 0.0f;
+    u32x4_t kbuf[2][4];
+    auto read_batch = [&](auto Bt, u32x4_t(&dst)[4]) {
+      static_for<0, 4>([&](auto J) {
+        dst[J] = *reinterpret_cast<const __attribute__((address_space(3)))
+                                       u32x4_t*>(krd[4 * Bt + J] + so);
+      });
+    };
+    read_batch(std::integral_constant<int, 0>{}, kbuf[0]);
+    static_for<0, 4>([&](auto Bt) {
+      if constexpr (Bt + 1 < 4)
+        read_batch(std::integral_constant<int, Bt + 1>{}, kbuf[(Bt + 1) & 1]);
+      static_for<0, 4>([&](auto J) {
+        constexpr int C = 4 * Bt + J;
+        static_for<0, 4>([&](auto I) {
+          constexpr int pr = 4 * C + I;
+          static_for<0, HW>([&](auto HL) {
+            constexpr int ii = I, bb = Bt & 1, jj = J, hh = HL;
+            acc[hh][ii % NACC] = dot2_bf16_bcast<HL * LPH + pr / PPL>(
+                qv[pr % PPL], kbuf[bb][jj][ii], acc[hh][ii % NACC]);
+          });
+        });
+      });
+    });
+    const bool valid = k_begin + t * kDecTile + lane < k_end;
+    float s2[HW];
+    bool need = false;
+#pragma unroll
+    for (int hl = 0; hl < HW; ++hl) {
+      float a = acc[hl][0];
+#pragma unroll
+      for (int k = 1; k < NACC; ++k) a += acc[hl][k];
+      s2[hl] = valid ? a * p.scale_log2 : -INFINITY;
+      need |= s2[hl] > m[hl] + kTau;
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int hl = 0; hl < HW; ++hl) {
+        const float mn = fmaxf(m[hl], wave_max(s2[hl]));
+        const float alpha = fast_exp2(m[hl] - mn);
+        m[hl] = mn;
+        lsum[hl] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hl][e] *= alpha;
+      }
+    }
+    uint16_t* P16 = reinterpret_cast<uint16_t*>(Ps);
+#pragma unroll
+    for (int hl = 0; hl < HW; ++hl) {
+      const uint16_t pb = to_bf16(fast_exp2(s2[hl] - m[hl]));
+      lsum[hl] += __builtin_bit_cast(float, (uint32_t)pb << 16);
+      P16[(lane >> 1) * (2 * HW) + hl * 2 + (lane & 1)] = pb;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P visible to the wave
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- P.V over the four 16-key quarters of the tile
+    static_for<0, 4>([&](auto Q) {
+      // key pairs 8Q + 2kg and 8Q + 2kg + 1, 4 heads each
+      const u32x4_t pa = *reinterpret_cast<
+          const __attribute__((address_space(3))) u32x4_t*>(prd + Q * 128);
+      const u32x4_t pc = *reinterpret_cast<
+          const __attribute__((address_space(3))) u32x4_t*>(prd + Q * 128 + 16);
+      static_for<0, 8>([&](auto E) {
+        const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16_t*>(
+                vrd[E] + so + Q * 16 * 256));
+        const uint2 vw = __builtin_bit_cast(uint2, r);
+#pragma unroll
+        for (int hl = 0; hl < HW; ++hl) {
+          o[hl][E] = dot2_bf16(pa[hl], vw.x, o[hl][E]);
+          o[hl][E] = dot2_bf16(pc[hl], vw.y, o[hl][E]);
+        }
+      });
+    });
+  };
+
+  constexpr std::integral_constant<int, 0> S0{};
+  constexpr std::integral_constant<int, 1> S1{};
+  issue_tile(0, S0);
+  for (int t = 0; t < ntiles; t += 2) {
+    // tile t has landed (this wave's rows); the barrier publishes every
+    // wave's rows and frees the other slot, consumed in the last step
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < ntiles) issue_tile(t + 1, S1);
+    consume(t, S0);
+    if (t + 1 < ntiles) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t + 2 < ntiles) issue_tile(t + 2, S0);
+      consume(t + 1, S1);
+    }
+  }
+
+  // ---- reduce over the four key groups and the 64 key lanes, write
+#pragma unroll
+  for (int hl = 0; hl < HW; ++hl) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[hl][e] += __shfl_xor(o[hl][e], 16, 64);
+      o[hl][e] += __shfl_xor(o[hl][e], 32, 64);
+    }
+    lsum[hl] = wave_sum(lsum[hl]);
+  }
+  if (kg == 0) {
+#pragma unroll
+    for (int hl = 0; hl < HW; ++hl) {
+      float* dst = part + 2 * kGroup + (w * HW + hl) * kD + jl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[16 * e] = o[hl][e];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int hl = 0; hl < HW; ++hl) {
+      part[w * HW + hl] = m[hl];
+      part[kGroup + w * HW + hl] = lsum[hl];
+    }
+  }
+}
+
 // Merge the split partials of one (sequence, query head, quarter of the
 // head dimension): with M the largest split maximum,
 // o = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s.  256 threads = 8 float4
@@ -551,12 +882,8 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
                          0, s, p);
     return hipGetLastError();
   }
-  if (local)
-    hipLaunchKernelGGL((decode_kernel<true, 4, false>), dim3(p.units), block,
-                       0, s, p);
-  else
-    hipLaunchKernelGGL((decode_kernel<false, 4, false>), dim3(p.units), block,
-                       0, s, p);
+  if (local) return hipErrorInvalidValue;  // local layers use the narrow shape
+  hipLaunchKernelGGL(decode_wide_kernel, dim3(p.units), block, 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(B * kHq * 4), dim3(256), 0, s,
