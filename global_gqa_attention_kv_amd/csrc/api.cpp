@@ -13,10 +13,10 @@ namespace {
 // Wide decode launches aim for about this many workgroups so every compute
 // unit holds a few resident workgroups; each workgroup then streams several
 // tiles.
-// Global-layer decode: two wide-kernel workgroups fit a CU (66 KB of LDS
-// each), so 512 workgroups on 256 CUs run as one full round (a partial
-// second round would leave half the device idle at the end).
-constexpr int kDecodeTargetWGs = 512;
+// Global-layer decode: as many wide-kernel workgroups as fit the 256 CUs at
+// once, so the launch runs as one full round (a partial second round would
+// leave part of the device idle at the end).
+constexpr int kDecodeTargetWGs = 256 * kWideWGsPerCU;
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 

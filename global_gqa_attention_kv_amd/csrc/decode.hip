@@ -487,10 +487,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 //    register plus a constant.
 constexpr int kTileBytes = kDecTile * 256;    // one 64-key tile of K or V
 constexpr int kSlotBytes = 2 * kTileBytes;    // K tile, then V tile
-constexpr int kWideHW = 4;                    // query heads per wave
-constexpr int kWidePs = (kDecTile / 2) * kWideHW * 4;  // P bytes per wave
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 // Direct-to-LDS load of 16 bytes per lane from a per-lane address: lane l's
 // bytes land at LDS byte address lds + 16 l (lds wave-uniform).  Written as
@@ -524,19 +524,32 @@ __device__ __forceinline__ void dma16(const uint16_t* base, uint32_t off,
       : "v"(off), "s"(base), "s"(lds)
       : "memory");
 }
+// s_waitcnt vmcnt(N): at most N of this wave's vector memory operations
+// (here: ring loads) still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
 
-__global__ __launch_bounds__(kDecThreads, 2) void decode_wide_kernel(
+// WAVES waves share the 16 query heads (16 / WAVES each); RING tile slots.
+template <int WAVES, int RING>
+__global__ __launch_bounds__(64 * WAVES, 1) void decode_wide_kernel(
     const DecodeParams p) {
-  constexpr int HW = kWideHW;
-  constexpr int LPH = 16 / HW;       // lanes per head in the q broadcast rows
-  constexpr int PPL = 4 * HW;        // q pairs per lane
+  constexpr int NT = 64 * WAVES;
+  constexpr int HW = kGroup / WAVES;  // query heads per wave
+  constexpr int LPH = 16 / HW;        // lanes per head in the q broadcast rows
+  constexpr int PPL = 4 * HW;         // q pairs per lane
   constexpr int PF = kGroup * (kD + 2);
+  constexpr int RPW = kDecTile / WAVES;   // tile rows each wave loads
+  constexpr int LPT = RPW / 4;            // loads per K (or V) tile per wave
+  constexpr int PSW = (kDecTile / 2) * HW * 4;  // P bytes per wave
+  static_assert(HW == 2 || HW == 4, "P reads assume 2 or 4 heads per wave");
   __shared__ __attribute__((aligned(16)))
-  uint8_t smem[2 * kSlotBytes + 4 * kWidePs];
+  uint8_t smem[RING * kSlotBytes + WAVES * PSW];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* Ps = smem + 2 * kSlotBytes + w * kWidePs;
+  uint8_t* Ps = smem + RING * kSlotBytes + w * PSW;
 
   const int unit = blockIdx.x;
   if (unit >= p.units) return;
@@ -567,8 +580,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_wide_kernel(
   }
 
   if (!has_keys) {
-    for (int i = tid; i < PF; i += kDecThreads)
-      part[i] = i < kGroup ? -INFINITY : 0.0f;
+    for (int i = tid; i < PF; i += NT) part[i] = i < kGroup ? -INFINITY : 0.0f;
     return;
   }
 
@@ -595,37 +607,36 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_wide_kernel(
       qv[v + 3] = w4.w;
     }
   }
-  // The waits in the tile loop count only the tile loads, so the q loads
+  // The waits in the tile loop count only the ring loads, so the q loads
   // complete here.  Passing q through an (empty) asm also tells the
   // compiler the loads are done: it cannot see the waits inside asm and
   // would otherwise repeat a full vmcnt wait before every use in the loop.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmcnt<0>();
 #pragma unroll
   for (int v = 0; v < PPL; ++v) asm volatile("" : "+v"(qv[v]));
 
-  // Tile t -> slot t % 2.  Wave w fills rows 16w .. 16w+15 of the K and V
-  // tiles, four rows (1 KB) per load: lane l takes row 16w + 4i + l/16 and
-  // chunk slot l % 16.
+  // Tile t -> slot t % RING.  Wave w fills rows RPW w .. RPW (w+1) - 1 of
+  // the K and V tiles, four rows (1 KB) per load: lane l takes row
+  // RPW w + 4i + l/16 and chunk slot l % 16.
   const int rsub = lane >> 4, cs = lane & 15;
-  uint32_t kdma[4], vdma[4];  // byte offsets from the tile's first key
+  uint32_t kdma[LPT], vdma[LPT];  // byte offsets from the tile's first key
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * i + rsub;  // == row & 15
-    const uint32_t row = 16 * w + r;
-    kdma[i] = row * (kTokenElems * 2) + ((cs ^ r) << 4);
-    vdma[i] = row * (kTokenElems * 2) + ((cs ^ (2 * (r & 3))) << 4);
+  for (int i = 0; i < LPT; ++i) {
+    const int row = RPW * w + 4 * i + rsub;
+    kdma[i] = row * (kTokenElems * 2) + ((cs ^ (row & 15)) << 4);
+    vdma[i] = row * (kTokenElems * 2) + ((cs ^ (2 * (row & 3))) << 4);
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   auto issue_tile = [&](int t, auto SLOT) {
     const int kb = k_begin + t * kDecTile;
     const uint32_t kl = __builtin_amdgcn_readfirstlane(
-        lds_base + SLOT * kSlotBytes + w * 16 * 256);
+        lds_base + SLOT * kSlotBytes + w * RPW * 256);
     if (kb + kDecTile <= k_end && (!use_new || new_key >= kb + kDecTile)) {
       // a full tile of cached keys
       const uint16_t* kt = Kb + (int64_t)kb * kTokenElems;
       const uint16_t* vt = Vb + (int64_t)kb * kTokenElems;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < LPT; ++i) {
         dma16(kt, kdma[i], kl + i * 1024);
         dma16(vt, vdma[i], kl + kTileBytes + i * 1024);
       }
@@ -633,14 +644,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_wide_kernel(
       // the split's last tile: keys past its end repeat the last key (they
       // are masked), and the query's own key comes from k_new / v_new
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * i + rsub;
-        const int key = min(kb + 16 * w + r, k_end - 1);
+      for (int i = 0; i < LPT; ++i) {
+        const int row = RPW * w + 4 * i + rsub;
+        const int key = min(kb + row, k_end - 1);
         const bool fresh = use_new && key == new_key;
         const uint16_t* krow = fresh ? Kn : Kb + (int64_t)key * kTokenElems;
         const uint16_t* vrow = fresh ? Vn : Vb + (int64_t)key * kTokenElems;
-        dma16(krow + ((cs ^ r) << 3), kl + i * 1024);
-        dma16(vrow + ((cs ^ (2 * (r & 3))) << 3), kl + kTileBytes + i * 1024);
+        dma16(krow + ((cs ^ (row & 15)) << 3), kl + i * 1024);
+        dma16(vrow + ((cs ^ (2 * (row & 3))) << 3),
+              kl + kTileBytes + i * 1024);
       }
     }
   };
@@ -662,8 +674,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_wide_kernel(
   for (int c = 0; c < 16; ++c) krd[c] = lds_base + lane * 256 + ((c ^ jl) << 4);
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    vrd[e] = lds_base + kTileBytes + (4 * kg + je) * 256 + 32 * (e ^ je) + 8 * ja;
-  const uint32_t prd = (uint32_t)(uintptr_t)Ps + 32 * kg;
+    vrd[e] = lds_base + kTileBytes + (4 * kg + je) * 256 + 32 * (e ^ je) +
+             8 * ja;
+  // P words of key pairs 8q + 2kg and 8q + 2kg + 1
+  const uint32_t prd = (uint32_t)(uintptr_t)Ps + 2 * kg * HW * 4;
 
   auto consume = [&](int t, auto SLOT) {
     constexpr uint32_t so = SLOT * kSlotBytes;
@@ -677,8 +691,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_wide_kernel(
     u32x4_t kbuf[2][4];
     auto read_batch = [&](auto Bt, u32x4_t(&dst)[4]) {
       static_for<0, 4>([&](auto J) {
-        dst[J] = *reinterpret_cast<const __attribute__((address_space(3)))
-                                       u32x4_t*>(krd[4 * Bt + J] + so);
+        dst[J] = *reinterpret_cast<const lds_u32x4_t*>(krd[4 * Bt + J] + so);
       });
     };
     read_batch(std::integral_constant<int, 0>{}, kbuf[0]);
@@ -731,15 +744,26 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_wide_kernel(
 
     // ---- P.V over the four 16-key quarters of the tile
     static_for<0, 4>([&](auto Q) {
-      // key pairs 8Q + 2kg and 8Q + 2kg + 1, 4 heads each
-      const u32x4_t pa = *reinterpret_cast<
-          const __attribute__((address_space(3))) u32x4_t*>(prd + Q * 128);
-      const u32x4_t pc = *reinterpret_cast<
-          const __attribute__((address_space(3))) u32x4_t*>(prd + Q * 128 + 16);
+      uint32_t pa[HW], pc[HW];  // pairs 8Q + 2kg and 8Q + 2kg + 1
+      if constexpr (HW == 4) {
+        const u32x4_t x = *reinterpret_cast<const lds_u32x4_t*>(prd + Q * 128);
+        const u32x4_t y =
+            *reinterpret_cast<const lds_u32x4_t*>(prd + Q * 128 + 16);
+        static_for<0, 4>([&](auto H) {
+          constexpr int h = H;
+          pa[h] = x[h];
+          pc[h] = y[h];
+        });
+      } else {
+        const u32x4_t x = *reinterpret_cast<const lds_u32x4_t*>(prd + Q * 64);
+        pa[0] = x[0];
+        pa[1] = x[1];
+        pc[0] = x[2];
+        pc[1] = x[3];
+      }
       static_for<0, 8>([&](auto E) {
         const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16_t*>(
-                vrd[E] + so + Q * 16 * 256));
+            reinterpret_cast<lds_v4i16_t*>(vrd[E] + so + Q * 16 * 256));
         const uint2 vw = __builtin_bit_cast(uint2, r);
 #pragma unroll
         for (int hl = 0; hl < HW; ++hl) {
@@ -750,22 +774,27 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_wide_kernel(
     });
   };
 
-  constexpr std::integral_constant<int, 0> S0{};
-  constexpr std::integral_constant<int, 1> S1{};
-  issue_tile(0, S0);
-  for (int t = 0; t < ntiles; t += 2) {
-    // tile t has landed (this wave's rows); the barrier publishes every
-    // wave's rows and frees the other slot, consumed in the last step
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < ntiles) issue_tile(t + 1, S1);
-    consume(t, S0);
-    if (t + 1 < ntiles) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (t + 2 < ntiles) issue_tile(t + 2, S0);
-      consume(t + 1, S1);
-    }
+  static_for<0, RING - 1>([&](auto T) {
+    if (T < ntiles) issue_tile(T, T);
+  });
+  for (int t0 = 0; t0 < ntiles; t0 += RING) {
+    static_for<0, RING>([&](auto S) {
+      const int t = t0 + S;
+      if (t < ntiles) {
+        // tile t has landed (this wave's rows) once only the later tiles'
+        // loads are outstanding; the barrier publishes every wave's rows
+        // and frees the slot consumed in the previous step
+        const int later = min(RING - 2, ntiles - 1 - t);
+        static_for<0, RING - 1>([&](auto L) {
+          if (later == L) wait_vmcnt<L * 2 * LPT>();
+        });
+        __syncthreads();
+        if (t + RING - 1 < ntiles)
+          issue_tile(t + RING - 1,
+                     std::integral_constant<int, (S + RING - 1) % RING>{});
+        consume(t, S);
+      }
+    });
   }
 
   // ---- reduce over the four key groups and the 64 key lanes, write
@@ -883,7 +912,8 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
     return hipGetLastError();
   }
   if (local) return hipErrorInvalidValue;  // local layers use the narrow shape
-  hipLaunchKernelGGL(decode_wide_kernel, dim3(p.units), block, 0, s, p);
+  hipLaunchKernelGGL((decode_wide_kernel<kWideWaves, kWideRing>), dim3(p.units),
+                     dim3(64 * kWideWaves), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(B * kHq * 4), dim3(256), 0, s,

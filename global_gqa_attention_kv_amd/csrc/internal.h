@@ -37,6 +37,15 @@ hipError_t launch_kv_append(const AppendParams& p, int B, int count,
 // ---------------------------------------------------------------- decode
 constexpr int kDecTile = 64;               // keys per tile
 constexpr int kDecThreads = 256;           // 4 waves
+// Global-layer (wide) decode kernel: waves per workgroup (16 / waves query
+// heads each), tile slots in its LDS ring (32 KB each), and how many such
+// workgroups fit one CU.  Four waves with a two-slot ring, two workgroups
+// per CU, measured fastest: eight waves (two heads each) or a single
+// workgroup with a deeper ring lose more VALU efficiency than they gain in
+// loads in flight.
+constexpr int kWideWaves = 4;
+constexpr int kWideRing = 2;
+constexpr int kWideWGsPerCU = kWideRing <= 2 ? 2 : 1;
 
 // Two launch shapes share one kernel template:
 //  * wide: a workgroup serves all 16 query heads of its KV head (4 per wave)
