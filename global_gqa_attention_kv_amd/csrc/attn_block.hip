@@ -52,14 +52,33 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kTauB = 8.0f;
-constexpr int kKRow = 272;                  // bytes per key row of a K tile
-constexpr int kVRow = 136;                  // bytes per dim row of a V^T tile
-constexpr int kKsB = kBlkTile * kKRow;      // 17408
-constexpr int kVtB = kD * kVRow;            // 17408
+constexpr int kTileB = kBlkTile * 256;      // one 64-key tile of K or V
+constexpr int kSlotB = 2 * kTileB;          // K tile, then V tile
 constexpr int kPartRow = 132;               // floats: o[128], m, l, pad
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int e) {
-  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds + 16 l (lds wave-uniform).  Inline assembly, so the compiler
+// does not hold every later LDS read behind it; the caller waits
+// (s_waitcnt vmcnt) and publishes with a barrier.  M0 carries the LDS
+// address; it is saved and restored, with one wait state before the load.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+__device__ __forceinline__ void wait_vmcnt0() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 __device__ __forceinline__ int64_t ring_prior(int64_t pos0) {
@@ -91,18 +110,26 @@ __global__ __launch_bounds__(64) void rope_keys_kernel(const BlockParams p) {
   d32[c + 32] = y;
 }
 
-// QPW = 8: 256 threads, at least two waves per SIMD (two workgroups per CU);
-// QPW = 16: 512 threads, one workgroup per CU.
+// QPW = 8: 256 threads, two workgroups per CU (64 KB of LDS each);
+// QPW = 16: 512 threads.
+//
+// Tiles stream into a two-slot LDS ring with direct-to-LDS loads: tile t + 1
+// is in flight while tile t is consumed, and no VGPRs or VALU work stage
+// it.  Both tiles keep rows of 256 bytes (one key), their 16-byte chunks
+// XOR-swizzled per row: K chunk c of row r at slot c ^ (r & 15), so the 32
+// lanes reading one chunk of 32 consecutive keys hit distinct banks; V chunk
+// c at slot c ^ 2(r & 3).  The V^T operand of the P.V product is read with
+// ds_read_b64_tr_b16, which returns four consecutive keys of one dimension
+// per lane; the swizzle puts the four keys a 16-lane group reads on
+// different banks.
 template <int QPW, bool LOCAL, bool SPLIT, bool OUT_F32>
 __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
     const BlockParams p) {
   constexpr int WAVES = QPW / 2;
-  constexpr int NT = WAVES * 64;
   constexpr int ROWS = QPW * kGroup;
-  constexpr int KLOADS = kBlkTile * 16 / NT;         // 16-B K chunks/thread
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kKsB + kVtB];
-  uint8_t* Ks = smem;
-  uint8_t* Vt = smem + kKsB;
+  constexpr int RPW = kBlkTile / WAVES;   // tile rows each wave loads
+  constexpr int LPT = RPW / 4;            // 1-KB loads per K or V tile per wave
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kSlotB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,6 +184,13 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
 #pragma unroll
     for (int k = 0; k < 8; ++k) qreg[k] = __builtin_bit_cast(bf16x8_t, raw[k]);
   }
+  // The ring waits below count only the tile loads, so the q loads complete
+  // here; passing q through an (empty) asm tells the compiler they are done
+  // (it cannot see waits inside asm and would otherwise wait again before
+  // every use in the loop).
+  wait_vmcnt0();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(qreg[k]));
 
   const uint16_t* kc_base = p.k_cache + (int64_t)b * p.seq_stride + g * kD;
   const uint16_t* vc_base = p.v_cache + (int64_t)b * p.seq_stride + g * kD;
@@ -175,58 +209,41 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
     return vc_base + (LOCAL ? (j & (kW - 1)) : j) * kTokenElems;
   };
 
-  // V staging unit: KPU consecutive keys x 8 dims (one 16-byte chunk of
-  // each key); NT units cover the 64-key tile.
-  constexpr int KPU = kBlkTile * 16 / NT;  // 4 (256 threads) or 2 (512)
-  // native vectors (not the uint4 struct) so the registers are never copied
-  // through private memory
-  u32x4_t kreg[KLOADS];
-  uint4 vreg[KPU];
-  auto load_tile = [&](int t) {
+  // Wave w fills tile rows RPW w .. RPW (w+1) - 1, four rows (1 KB) per
+  // load: lane l takes row RPW w + 4i + l/16 and chunk slot l % 16.  Keys
+  // past the range repeat its last key (masked).
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+  const int rsub = lane >> 4, cs = lane & 15;
+  auto issue_tile = [&](int t, auto SLOT) {
     const int kb = k_lo + (t_begin + t) * kBlkTile;
-    static_for<0, KLOADS>([&](auto I) {
-      const int u = tid + I * NT;
-      const int key = u >> 4, c = u & 15;
-      const int j = min(kb + key, k_hi - 1);
-      kreg[I] = *reinterpret_cast<const u32x4_t*>(k_src(j) + c * 8);
-    });
-    const int kq = tid >> 4, c = tid & 15;
-    static_for<0, KPU>([&](auto R) {
-      const int j = min(kb + KPU * kq + R, k_hi - 1);
-      vreg[R] = *reinterpret_cast<const uint4*>(v_src(j) + c * 8);
-    });
+    const uint32_t kl = __builtin_amdgcn_readfirstlane(
+        lds_base + SLOT * kSlotB + w * RPW * 256);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int r = RPW * w + 4 * i + rsub;
+      const int j = min(kb + r, k_hi - 1);
+      dma16(k_src(j) + ((cs ^ (r & 15)) << 3), kl + i * 1024);
+      dma16(v_src(j) + ((cs ^ (2 * (r & 3))) << 3), kl + kTileB + i * 1024);
+    }
   };
-  auto store_tile = [&]() {
-    static_for<0, KLOADS>([&](auto I) {
-      const int u = tid + I * NT;
-      const int key = u >> 4, c = u & 15;
-      *reinterpret_cast<u32x4_t*>(Ks + key * kKRow + c * 16) = kreg[I];
-    });
-    // V^T rows are stored with the 8-byte (4-key) units XOR-swizzled by
-    // (dim / 8): without it the 16 lanes of a write group, which hold dims
-    // 8c + e for c = 0..15, would hit only 4 bank groups.
-    const int kq = tid >> 4, c = tid & 15;
-    static_for<0, 4>([&](auto E) {
-      // dims 8c+2e and 8c+2e+1 of keys KPU*kq .. KPU*kq+KPU-1
-      const int unit = (KPU * kq) >> 2;          // 8-byte unit of the keys
-      const int sub = (KPU * kq) & 3;            // key offset inside it
-      uint8_t* even =
-          Vt + (8 * c + 2 * E) * kVRow + ((unit ^ c) << 3) + 2 * sub;
-      uint8_t* odd = even + kVRow;
-      if constexpr (KPU == 4) {
-        const uint32_t w0 = word(vreg[0], E), w1 = word(vreg[1], E);
-        const uint32_t w2 = word(vreg[2], E), w3 = word(vreg[3], E);
-        *reinterpret_cast<uint2*>(even) =
-            make_uint2(interleave_lo(w0, w1), interleave_lo(w2, w3));
-        *reinterpret_cast<uint2*>(odd) =
-            make_uint2(interleave_hi(w0, w1), interleave_hi(w2, w3));
-      } else {
-        const uint32_t w0 = word(vreg[0], E), w1 = word(vreg[1], E);
-        *reinterpret_cast<uint32_t*>(even) = interleave_lo(w0, w1);
-        *reinterpret_cast<uint32_t*>(odd) = interleave_hi(w0, w1);
-      }
-    });
-  };
+
+  // LDS read addresses.  K operand of k-step k: key 32be + row, chunk
+  // 2k + hi5 (+ 8192 B for be = 1).  V^T operand of dim block d: the
+  // 16-lane group G (keys + 4(G >> 1), dims + 16(G & 1)) transposes keys
+  // 16c + 4(G >> 1) + e, e = (lane & 15) >> 2, at dims 32d + 16(G & 1) +
+  // 4((lane & 15) & 3); keys + 8 are 2048 B further.
+  uint32_t krd[8], vrd[4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    krd[k] = lds_base + row * 256 + (((2 * k + hi5) ^ (row & 15)) << 4);
+  {
+    const int G = lane >> 4, jl = lane & 15, ja = jl & 3, je = jl >> 2;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      vrd[d] = lds_base + kTileB + (4 * (G >> 1) + je) * 256 +
+               (((4 * d + 2 * (G & 1) + (ja >> 1)) ^ (2 * je)) << 4) +
+               8 * (ja & 1);
+  }
 
   f32x16_t O[4];
 #pragma unroll
@@ -235,12 +252,8 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
     for (int i = 0; i < 16; ++i) O[d][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  if (ntiles > 0) load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
-
+  auto consume = [&](int t, auto SLOT) {
+    constexpr uint32_t so = SLOT * kSlotB;
     // ---- S^T = K Q^T for two 32-key blocks
     f32x16_t S[2];
 #pragma unroll
@@ -249,8 +262,8 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
       for (int i = 0; i < 16; ++i) S[be][i] = 0.0f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            Ks + (32 * be + row) * kKRow + (2 * k + hi5) * 16);
+        const bf16x8_t a =
+            *reinterpret_cast<const lds_bf16x8_t*>(krd[k] + so + be * 8192);
         S[be] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[k], S[be], 0,
                                                         0, 0);
       }
@@ -317,21 +330,39 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
     // ---- O^T += V^T P^T over four 16-key steps, four 32-dim blocks
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      // keys 16c + 4 hi5 + 0..3 and + 8..11: 8-byte units u0 and u0 + 2
-      const int u0 = 4 * c + hi5;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const int dim = 32 * d + row, sw = dim >> 3;
-        const uint8_t* vr = Vt + dim * kVRow;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + ((u0 ^ sw) << 3));
-        const uint2 hi =
-            *reinterpret_cast<const uint2*>(vr + (((u0 + 2) ^ sw) << 3));
-        const uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, a4), P[c], O[d], 0, 0, 0);
+        // keys 16c + 4 hi5 + 0..3, then + 8..11, at this lane's dimension
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_v4i16_t*>(vrd[d] + so + c * 4096));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_v4i16_t*>(vrd[d] + so + c * 4096 + 2048));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo);
+        const uint2 h2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8_t a4 = __builtin_bit_cast(
+            bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+        O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a4, P[c], O[d], 0, 0,
+                                                       0);
       }
     }
+  };
+
+  constexpr std::integral_constant<int, 0> S0{};
+  constexpr std::integral_constant<int, 1> S1{};
+  if (ntiles > 0) issue_tile(0, S0);
+  for (int t = 0; t < ntiles; t += 2) {
+    // tile t has landed (this wave's rows); the barrier publishes every
+    // wave's rows and frees the other slot, consumed in the last step
+    wait_vmcnt0();
     __syncthreads();
+    if (t + 1 < ntiles) issue_tile(t + 1, S1);
+    consume(t, S0);
+    if (t + 1 < ntiles) {
+      wait_vmcnt0();
+      __syncthreads();
+      if (t + 2 < ntiles) issue_tile(t + 2, S0);
+      consume(t + 1, S1);
+    }
   }
 
   // ---- epilogue: this lane holds row `row`, dims 32d + 8(i>>2) + 4 hi5 + i&3
