@@ -118,10 +118,10 @@ __global__ __launch_bounds__(64) void rope_keys_kernel(const BlockParams p) {
 // it.  Both tiles keep rows of 256 bytes (one key), their 16-byte chunks
 // XOR-swizzled per row: K chunk c of row r at slot c ^ (r & 15), so the 32
 // lanes reading one chunk of 32 consecutive keys hit distinct banks; V chunk
-// c at slot c ^ 2(r & 3).  The V^T operand of the P.V product is read with
-// ds_read_b64_tr_b16, which returns four consecutive keys of one dimension
-// per lane; the swizzle puts the four keys a 16-lane group reads on
-// different banks.
+// c at slot c ^ X(r & 3), X = {0, 4, 10, 14}.  The V^T operand of the P.V
+// product is read with ds_read_b64_tr_b16, which returns four consecutive
+// keys of one dimension per lane; X puts the four keys of a 16-lane group,
+// and the 64 bytes of each key read by a 32-lane half, on distinct banks.
 template <int QPW, bool LOCAL, bool SPLIT, bool OUT_F32>
 __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
     const BlockParams p) {
@@ -214,6 +214,7 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
   // past the range repeat its last key (masked).
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   const int rsub = lane >> 4, cs = lane & 15;
+  auto vswz = [](int r) { return 4 * (r & 3) + 2 * ((r >> 1) & 1); };
   auto issue_tile = [&](int t, auto SLOT) {
     const int kb = k_lo + (t_begin + t) * kBlkTile;
     const uint32_t kl = __builtin_amdgcn_readfirstlane(
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
       const int r = RPW * w + 4 * i + rsub;
       const int j = min(kb + r, k_hi - 1);
       dma16(k_src(j) + ((cs ^ (r & 15)) << 3), kl + i * 1024);
-      dma16(v_src(j) + ((cs ^ (2 * (r & 3))) << 3), kl + kTileB + i * 1024);
+      dma16(v_src(j) + ((cs ^ vswz(r)) << 3), kl + kTileB + i * 1024);
     }
   };
 
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
 #pragma unroll
     for (int d = 0; d < 4; ++d)
       vrd[d] = lds_base + kTileB + (4 * (G >> 1) + je) * 256 +
-               (((4 * d + 2 * (G & 1) + (ja >> 1)) ^ (2 * je)) << 4) +
+               (((4 * d + 2 * (G & 1) + (ja >> 1)) ^ vswz(je)) << 4) +
                8 * (ja & 1);
   }
 
