@@ -255,20 +255,53 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
 
   auto consume = [&](int t, auto SLOT) {
     constexpr uint32_t so = SLOT * kSlotB;
-    // ---- S^T = K Q^T for two 32-key blocks
+    // ---- S^T = K Q^T for two 32-key blocks.  The K operands of block 0 are
+    // all requested before its first product and those of block 1 while
+    // block 0 multiplies, so no product waits on a fresh LDS read.
     f32x16_t S[2];
 #pragma unroll
-    for (int be = 0; be < 2; ++be) {
+    for (int be = 0; be < 2; ++be)
 #pragma unroll
       for (int i = 0; i < 16; ++i) S[be][i] = 0.0f;
+    bf16x8_t ka[2][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const bf16x8_t a =
-            *reinterpret_cast<const lds_bf16x8_t*>(krd[k] + so + be * 8192);
-        S[be] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[k], S[be], 0,
-                                                        0, 0);
-      }
+    for (int k = 0; k < 8; ++k)
+      ka[0][k] = *reinterpret_cast<const lds_bf16x8_t*>(krd[k] + so);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][k], qreg[k], S[0],
+                                                     0, 0, 0);
+      ka[1][k] = *reinterpret_cast<const lds_bf16x8_t*>(krd[k] + so + 8192);
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][k], qreg[k], S[1],
+                                                     0, 0, 0);
+    // The V^T operands of the first 16-key step of P.V are requested
+    // meanwhile (they do not depend on the softmax).
+    constexpr uint32_t vo = so;  // vrd[] already points into the V tile
+    v4i16_t vt[2][4][2];  // [step parity][dim block][keys +0..3 | +8..11]
+    auto read_vt = [&](int c, v4i16_t(&dst)[4][2]) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        dst[d][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_v4i16_t*>(vrd[d] + vo + c * 4096));
+        dst[d][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_v4i16_t*>(vrd[d] + vo + c * 4096 + 2048));
+      }
+    };
+    read_vt(0, vt[0]);
+    // issue order: 8 reads, then (product, read) x 8, then the 8 block-1
+    // products interleaved with the 8 V^T reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    static_for<0, 8>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+    static_for<0, 8>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
 
     // ---- softmax update for this lane's row.  The maximum is taken on raw
     // scores (the scale is positive) and the scale is folded into the
@@ -328,24 +361,29 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
             bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
       }
 
-    // ---- O^T += V^T P^T over four 16-key steps, four 32-dim blocks
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    // ---- O^T += V^T P^T over four 16-key steps, four 32-dim blocks; the
+    // operands of step c + 1 are read while step c multiplies
+    static_for<0, 4>([&](auto C) {
+      constexpr int c = C;
+      if constexpr (c + 1 < 4) read_vt(c + 1, vt[(c + 1) & 1]);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         // keys 16c + 4 hi5 + 0..3, then + 8..11, at this lane's dimension
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<lds_v4i16_t*>(vrd[d] + so + c * 4096));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<lds_v4i16_t*>(vrd[d] + so + c * 4096 + 2048));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo);
-        const uint2 h2 = __builtin_bit_cast(uint2, hi);
+        const uint2 l2 = __builtin_bit_cast(uint2, vt[c & 1][d][0]);
+        const uint2 h2 = __builtin_bit_cast(uint2, vt[c & 1][d][1]);
         const bf16x8_t a4 = __builtin_bit_cast(
             bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
         O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a4, P[c], O[d], 0, 0,
                                                        0);
       }
-    }
+    });
+    static_for<0, 3>([&](auto) {
+      static_for<0, 4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      });
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
 
   constexpr std::integral_constant<int, 0> S0{};
