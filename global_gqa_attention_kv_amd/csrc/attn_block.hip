@@ -54,6 +54,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kTauB = 8.0f;
 constexpr int kTileB = kBlkTile * 256;      // one 64-key tile of K or V
 constexpr int kSlotB = 2 * kTileB;          // K tile, then V tile
+template <int QPW>
+constexpr int kBlockRing = QPW == 16 ? 3 : 2;  // tile slots in LDS
 constexpr int kPartRow = 132;               // floats: o[128], m, l, pad
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -79,6 +81,12 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
 }
 __device__ __forceinline__ void wait_vmcnt0() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+// s_waitcnt vmcnt(N): at most N of this wave's vector memory operations
+// (here: tile loads) still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 }
 
 __device__ __forceinline__ int64_t ring_prior(int64_t pos0) {
@@ -110,8 +118,10 @@ __global__ __launch_bounds__(64) void rope_keys_kernel(const BlockParams p) {
   d32[c + 32] = y;
 }
 
-// QPW = 8: 256 threads, two workgroups per CU (64 KB of LDS each);
-// QPW = 16: 512 threads.
+// QPW = 8: 256 threads, a two-slot ring, two workgroups per CU (64 KB of
+// LDS each).  QPW = 16: 512 threads (two waves per SIMD from one
+// workgroup) sharing each tile among twice the rows, so a CU needs half the
+// tile traffic, with a three-slot ring (96 KB) that loads two tiles ahead.
 //
 // Tiles stream into a two-slot LDS ring with direct-to-LDS loads: tile t + 1
 // is in flight while tile t is consumed, and no VGPRs or VALU work stage
@@ -123,13 +133,14 @@ __global__ __launch_bounds__(64) void rope_keys_kernel(const BlockParams p) {
 // keys of one dimension per lane; X puts the four keys of a 16-lane group,
 // and the 64 bytes of each key read by a 32-lane half, on distinct banks.
 template <int QPW, bool LOCAL, bool SPLIT, bool OUT_F32>
-__global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
+__global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
     const BlockParams p) {
   constexpr int WAVES = QPW / 2;
+  constexpr int RING = kBlockRing<QPW>;
   constexpr int ROWS = QPW * kGroup;
   constexpr int RPW = kBlkTile / WAVES;   // tile rows each wave loads
   constexpr int LPT = RPW / 4;            // 1-KB loads per K or V tile per wave
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kSlotB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[RING * kSlotB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -386,22 +397,29 @@ __global__ __launch_bounds__(QPW * 32, 2) void block_attn_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
 
-  constexpr std::integral_constant<int, 0> S0{};
-  constexpr std::integral_constant<int, 1> S1{};
-  if (ntiles > 0) issue_tile(0, S0);
-  for (int t = 0; t < ntiles; t += 2) {
-    // tile t has landed (this wave's rows); the barrier publishes every
-    // wave's rows and frees the other slot, consumed in the last step
-    wait_vmcnt0();
-    __syncthreads();
-    if (t + 1 < ntiles) issue_tile(t + 1, S1);
-    consume(t, S0);
-    if (t + 1 < ntiles) {
-      wait_vmcnt0();
-      __syncthreads();
-      if (t + 2 < ntiles) issue_tile(t + 2, S0);
-      consume(t + 1, S1);
-    }
+  // tile t -> slot t % RING, loaded RING - 1 tiles ahead; the loop is
+  // unrolled RING times so every slot offset is a constant
+  static_for<0, RING - 1>([&](auto T) {
+    if (T < ntiles) issue_tile(T, T);
+  });
+  for (int t0 = 0; t0 < ntiles; t0 += RING) {
+    static_for<0, RING>([&](auto S) {
+      const int t = t0 + S;
+      if (t < ntiles) {
+        // tile t has landed (this wave's rows) once only the later tiles'
+        // loads are outstanding; the barrier publishes every wave's rows
+        // and frees the slot consumed in the previous step
+        const int later = min(RING - 2, ntiles - 1 - t);
+        static_for<0, RING - 1>([&](auto L) {
+          if (later == L) wait_vmcnt<L * 2 * LPT>();
+        });
+        __syncthreads();
+        if (t + RING - 1 < ntiles)
+          issue_tile(t + RING - 1,
+                     std::integral_constant<int, (S + RING - 1) % RING>{});
+        consume(t, S);
+      }
+    });
   }
 
   // ---- epilogue: this lane holds row `row`, dims 32d + 8(i>>2) + 4 hi5 + i&3
