@@ -55,7 +55,7 @@ constexpr float kTauB = 8.0f;
 constexpr int kTileB = kBlkTile * 256;      // one 64-key tile of K or V
 constexpr int kSlotB = 2 * kTileB;          // K tile, then V tile
 template <int QPW>
-constexpr int kBlockRing = QPW == 16 ? 3 : 2;  // tile slots in LDS
+constexpr int kBlockRing = QPW == 16 ? 4 : 2;  // tile slots in LDS
 constexpr int kPartRow = 132;               // floats: o[128], m, l, pad
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
