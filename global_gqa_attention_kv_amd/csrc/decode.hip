@@ -9,40 +9,46 @@
 // RoPE on a local layer.
 //
 // Design (gfx950, VALU; decode is a streaming read of the cache):
-//  * One workgroup of 256 threads owns one (sequence, KV head, key split) and
-//    serves all 16 query heads of that KV head, so each cached K/V byte is
-//    fetched from HBM exactly once.
-//  * Keys stream through LDS in tiles of 64.  Every thread prefetches its
-//    share of the next tile with 16-byte coalesced loads while the current
-//    tile is being consumed.  K rows are stored with an XOR swizzle of their
-//    16-byte chunks so a lane can read a whole row without bank conflicts; V
-//    is re-packed into (key 2i, key 2i+1) bf16 pairs on the way in so the P.V
-//    product can use the packed-pair dot instruction.
-//  * Q.K: lane = key, each wave takes 4 of the 16 heads; the query words are
-//    wave-uniform and come straight from the scalar cache as SGPR operands of
-//    v_dot2_f32_bf16 (bf16 products exact, fp32 accumulation).
+//  * A workgroup owns one (sequence, KV head, key split) and serves query
+//    heads of that KV head out of the same tiles, so each cached K/V byte is
+//    fetched from HBM once per workgroup that needs it.
+//  * Keys stream through LDS in tiles of 64.  K rows sit with an XOR swizzle
+//    of their 16-byte chunks so a lane can read a whole row without bank
+//    conflicts.
+//  * Q.K: lane = key; the query words are wave-uniform, held 16 to a VGPR
+//    and broadcast with DPP row_newbcast into v_dot2c_f32_bf16 (bf16
+//    products exact, fp32 accumulation).
 //  * Online softmax in the log2 domain with a lazy maximum: the running
 //    maximum is only raised (and the accumulators rescaled) when some score
 //    exceeds it by more than 2^8, which keeps every exponent <= 2^8 while
-//    skipping nearly all cross-lane reductions.
-//  * P.V: each wave accumulates its 4 heads x 128 dims; lane = (8 dims, one
-//    of 4 key-pair groups); P is stored to wave-private LDS as bf16 pairs.
-//  * Local layers rotate each key by its offset to the query (j - i) before
-//    it reaches LDS; since <R_i q, R_j k> = <q, R_{j-i} k> the query stays
-//    unrotated and the angles stay small (|j - i| < 2048), so fp32 angle
-//    arithmetic keeps ~1e-4 rad accuracy.
-//  * Each workgroup writes (m, l, o) for its split.  Global layers (large
-//    caches) use the 16-head shape above and a second, fully parallel merge
-//    kernel.  Local layers (2048 keys, latency-bound) use a narrow shape: 4
-//    heads (one per wave) and one tile per workgroup, the four head groups of
-//    a tile placed on one XCD so they share its L2, and the last workgroup of
-//    each (sequence, KV head, head group) -- found with a device-scope
-//    counter in the workspace -- merges the splits in the same launch.  The
-//    partials travel with device-scope (write-through) stores and loads, so
-//    no workgroup has to write back its whole L2.
+//    skipping nearly all cross-lane reductions.  The denominator sums exactly
+//    the bf16 weights the P.V product uses.
+//  * P.V: P goes to wave-private LDS as bf16 key pairs; each lane
+//    accumulates 8 dimensions of its wave's heads over a quarter of the
+//    tile's key pairs with the packed-pair dot; the quarters are summed at
+//    the end.
+//  * Each workgroup writes (m, l, o) for its split; the splits are merged
+//    with the log-sum-exp rule.
 //  * Optionally the call appends the query's own K/V: the kernel reads that
 //    key from the new-token buffers and one workgroup stores it to its slot,
 //    saving a separate append launch per layer.
+//
+// Two kernels:
+//  * decode_wide_kernel (global layers, long caches): all 16 heads per
+//    workgroup (4 per wave), direct-to-LDS tile loads into a two-slot ring,
+//    V read back transposed (see the kernel); a second kernel merges.
+//  * decode_kernel (local layers, 2048-key windows, latency-bound): 4 heads
+//    per workgroup (one per wave), one or two tiles per workgroup; tiles are
+//    staged through VGPRs so each key is rotated by its offset to the query
+//    (j - i) on its way into LDS -- <R_i q, R_j k> = <q, R_{j-i} k>, so the
+//    query stays unrotated and the angles stay small (|j - i| < 2048; fp32
+//    angle error ~1e-4 rad) -- and V is re-packed into (key 2i, key 2i+1)
+//    pairs.  The four head groups of a tile are placed on one XCD so they
+//    share its L2, and the last workgroup of each (sequence, KV head, head
+//    group), found with a device-scope counter in the workspace, merges the
+//    splits in the same launch.  The partials travel with device-scope
+//    (write-through) stores and loads, so no workgroup has to write back its
+//    whole L2.
 #include "device_common.h"
 #include "internal.h"
 

@@ -47,15 +47,16 @@ constexpr int kWideWaves = 4;
 constexpr int kWideRing = 2;
 constexpr int kWideWGsPerCU = kWideRing <= 2 ? 2 : 1;
 
-// Two launch shapes share one kernel template:
-//  * wide: a workgroup serves all 16 query heads of its KV head (4 per wave)
-//    and a long key split; a separate kernel merges the splits.  Used where
-//    the cache is large (global layers).
-//  * narrow: a workgroup serves 4 query heads (1 per wave) and a single
-//    tile; the four head groups of one tile run on the same XCD so three of
-//    them hit L2, and the last workgroup of each (sequence, KV head, head
-//    group) merges the splits in the same launch.  Used for the 2048-key
-//    local windows, where latency rather than bandwidth sets the time.
+// Two launch shapes:
+//  * wide (decode_wide_kernel): a workgroup serves all 16 query heads of its
+//    KV head and a long key split; a separate kernel merges the splits.
+//    Used where the cache is large (global layers).
+//  * narrow (decode_kernel): a workgroup serves 4 query heads (1 per wave)
+//    and one or two tiles; the four head groups of one tile run on the same
+//    XCD so three of them hit L2, and the last workgroup of each (sequence,
+//    KV head, head group) merges the splits in the same launch.  Used for
+//    the 2048-key local windows, where latency rather than bandwidth sets
+//    the time.
 struct DecodePlan {
   bool narrow;
   int heads_per_wg;     // 16 (wide) or 4 (narrow)
