@@ -273,8 +273,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             constexpr int pr = 4 * C + I;
             static_for<0, HW>([&](auto HL) {
               constexpr int ii = I, bb = Bt & 1, jj = J, hh = HL;
-              acc[hh][ii % NACC] = dot2_bf16_bcast<HL * LPH + pr / PPL>(
-                  qv[pr % PPL], kbuf[bb][jj][ii], acc[hh][ii % NACC]);
+              acc[hh][ii % NACC] =
+                  dot2_bf16_bcast<HL * LPH + pr / PPL, (C == 0 && ii < NACC)>(
+                      qv[pr % PPL], kbuf[bb][jj][ii], acc[hh][ii % NACC]);
             });
           });
         });
@@ -481,11 +482,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 //  * K rows keep the narrow shape's layout: 16-byte chunk c of key row r sits
 //    at chunk slot c ^ (r & 15) (the lane that fills slot s fetches chunk
 //    s ^ (r & 15)), so lane = key reads its whole row conflict-free.
-//  * V rows stay in key order with chunk c at slot c ^ 2(r & 3).  The P.V
+//  * V rows stay in key order with chunk c at slot c ^ 2(r & 7).  The P.V
 //    operands are read with ds_read_b64_tr_b16, which gives each lane four
 //    consecutive keys of one dimension: two key-interleaved bf16 pairs, the
 //    operand v_dot2_f32_bf16 wants, with no VALU re-packing.  The XOR puts
-//    the four keys read by each 16-lane group on different banks.
+//    the eight keys read by each 32-lane half on different banks.
 //  * P.V lanes: lane 16 g + j owns dimensions j, j + 16, ..., j + 112 of its
 //    wave's 4 heads and keys 16 q + 4 g .. + 3 of each 16-key quarter q; the
 //    four groups g are summed at the end.
@@ -630,7 +631,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_wide_kernel(
   for (int i = 0; i < LPT; ++i) {
     const int row = RPW * w + 4 * i + rsub;
     kdma[i] = row * (kTokenElems * 2) + ((cs ^ (row & 15)) << 4);
-    vdma[i] = row * (kTokenElems * 2) + ((cs ^ (2 * (row & 3))) << 4);
+    vdma[i] = row * (kTokenElems * 2) + ((cs ^ (2 * (row & 7))) << 4);
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   auto issue_tile = [&](int t, auto SLOT) {
@@ -657,7 +658,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_wide_kernel(
         const uint16_t* krow = fresh ? Kn : Kb + (int64_t)key * kTokenElems;
         const uint16_t* vrow = fresh ? Vn : Vb + (int64_t)key * kTokenElems;
         dma16(krow + ((cs ^ (row & 15)) << 3), kl + i * 1024);
-        dma16(vrow + ((cs ^ (2 * (row & 3))) << 3),
+        dma16(vrow + ((cs ^ (2 * (row & 7))) << 3),
               kl + kTileBytes + i * 1024);
       }
     }
@@ -680,7 +681,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_wide_kernel(
   for (int c = 0; c < 16; ++c) krd[c] = lds_base + lane * 256 + ((c ^ jl) << 4);
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    vrd[e] = lds_base + kTileBytes + (4 * kg + je) * 256 + 32 * (e ^ je) +
+    vrd[e] = lds_base + kTileBytes + (4 * kg + je) * 256 +
+             32 * (e ^ ((4 * kg + je) & 7)) +
              8 * ja;
   // P words of key pairs 8q + 2kg and 8q + 2kg + 1
   const uint32_t prd = (uint32_t)(uintptr_t)Ps + 2 * kg * HW * 4;
@@ -710,8 +712,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_wide_kernel(
           constexpr int pr = 4 * C + I;
           static_for<0, HW>([&](auto HL) {
             constexpr int ii = I, bb = Bt & 1, jj = J, hh = HL;
-            acc[hh][ii % NACC] = dot2_bf16_bcast<HL * LPH + pr / PPL>(
-                qv[pr % PPL], kbuf[bb][jj][ii], acc[hh][ii % NACC]);
+            acc[hh][ii % NACC] =
+                dot2_bf16_bcast<HL * LPH + pr / PPL, (C == 0 && ii < NACC)>(
+                    qv[pr % PPL], kbuf[bb][jj][ii], acc[hh][ii % NACC]);
           });
         });
       });

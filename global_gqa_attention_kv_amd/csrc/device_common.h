@@ -22,16 +22,25 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // k).  The DPP row_newbcast operand lets 16 distinct wave-uniform words live
 // in one VGPR (replicated in the four rows) instead of SGPRs.  Hazard: none
 // of q, k, acc may have been written by either of the two VALU instructions
-// before this one (the compiler cannot see that the asm is a DPP op); the
-// callers interleave independent accumulators, and a host test checks the
-// generated code.
-template <int LANE>
+// before this one (the compiler cannot see that the asm is a DPP op).  The
+// callers interleave independent accumulators, so a product's accumulator
+// was last written four products earlier; the first product of each
+// accumulator (FIRST), whose accumulator was just initialised, carries its
+// own two wait states.  A host test checks the generated code.
+template <int LANE, bool FIRST = false>
 __device__ __forceinline__ float dot2_bf16_bcast(uint32_t q, uint32_t k,
                                                  float acc) {
-  asm("v_dot2c_f32_bf16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf "
-      "bank_mask:0xf"
-      : "+v"(acc)
-      : "v"(q), "v"(k), "i"(LANE));
+  if constexpr (FIRST)
+    asm("s_nop 1\n\t"
+        "v_dot2c_f32_bf16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf "
+        "bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(q), "v"(k), "i"(LANE));
+  else
+    asm("v_dot2c_f32_bf16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf "
+        "bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(q), "v"(k), "i"(LANE));
   return acc;
 }
 
