@@ -76,6 +76,9 @@ BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify) {
   if (groups < kBlockTargetWGs)
     splits = (kBlockTargetWGs + groups - 1) / groups;
   if (splits > tiles) splits = tiles;
+  // at least two tiles per workgroup: a split's fixed costs (Q load and
+  // rotation, ring fill, partial write) outweigh a single tile
+  if (splits > 1 && splits > tiles / 2) splits = tiles / 2 > 1 ? tiles / 2 : 1;
   if (splits < 1) splits = 1;
   p.splits = (int)splits;
   p.klin_bytes = kind == GQA_LOCAL
