@@ -61,6 +61,16 @@ def test_decode_full_context_131072(kind):
     check_close(got, want, "decode ctx131072 kind=%d" % kind)
 
 
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_decode_max_batch_64(kind):
+    # the largest batch the library takes, ragged positions up to 6000:
+    # the planner's smallest split count per sequence
+    positions = [int(x) for x in np.random.default_rng(64).integers(0, 6000, 64)]
+    positions[0], positions[-1] = 0, 5999
+    got, want, _, _ = _decode_case(kind, positions, seed=1010)
+    check_close(got, want, "decode B=64 kind=%d" % kind)
+
+
 def test_decode_batch4_131072_global():
     positions = [131071, 131071, 100000, 77777]
     got, want, _, _ = _decode_case(ga.GLOBAL, positions, seed=1004,
