@@ -314,6 +314,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-extras", action="store_true",
                     help="decode step only (skip verify and prefill)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the chunked-prefill measurement and print "
+                         "its JSON (for hardware-counter runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB, "
                          "to scale hardware byte counters")
@@ -327,6 +330,9 @@ def main():
     import torch
     ga = _ensure_built()
     torch.cuda.set_device(0)
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill(ga, torch)}), flush=True)
+        return
     if args.calibrate_copy_mib:
         nbytes = args.calibrate_copy_mib << 20
         src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
