@@ -186,11 +186,33 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       raw[k] = *reinterpret_cast<const uint4*>(qrow + 16 * k);
-    if (LOCAL) {
-      const float delta = (float)qic;
+    // q is rotated (local layers) and multiplied by scale * log2(e) in fp32,
+    // then rounded to bf16 once: the products then come out in log2 units
+    // and the softmax needs no per-score multiply
+    const float c = p.scale_log2;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        rope_rotate(raw[k], raw[k + 4], delta, p.rope_rev + 16 * k + 8 * hi5);
+    for (int k = 0; k < 4; ++k) {
+      uint32_t* lo = reinterpret_cast<uint32_t*>(&raw[k]);
+      uint32_t* hi = reinterpret_cast<uint32_t*>(&raw[k + 4]);
+      const float* rev = p.rope_rev + 16 * k + 8 * hi5;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x0 = bf16_lo(lo[e]), x1 = bf16_hi(lo[e]);
+        float y0 = bf16_lo(hi[e]), y1 = bf16_hi(hi[e]);
+        if (LOCAL) {
+          float r0 = (float)qic * rev[2 * e], r1 = (float)qic * rev[2 * e + 1];
+          r0 -= rintf(r0);
+          r1 -= rintf(r1);
+          float s0, c0, s1, c1;
+          sincos_rev(r0, &s0, &c0);
+          sincos_rev(r1, &s1, &c1);
+          const float a0 = x0 * c0 - y0 * s0, a1 = x1 * c1 - y1 * s1;
+          const float b0 = y0 * c0 + x0 * s0, b1 = y1 * c1 + x1 * s1;
+          x0 = a0, x1 = a1, y0 = b0, y1 = b1;
+        }
+        lo[e] = pack_bf16(x0 * c, x1 * c);
+        hi[e] = pack_bf16(y0 * c, y1 * c);
+      }
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) qreg[k] = __builtin_bit_cast(bf16x8_t, raw[k]);
@@ -269,11 +291,16 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
     // ---- S^T = K Q^T for two 32-key blocks.  The K operands of block 0 are
     // all requested before its first product and those of block 1 while
     // block 0 multiplies, so no product waits on a fresh LDS read.
+    // The accumulators start at -mb (mb: the row's running maximum, 0 while
+    // it has none), so they end up holding s - mb in log2 units.
+    // a row that has seen no visible key yet keeps m = -inf; any finite
+    // base then turns its -inf scores into zero weights
+    const float mb = m_run == -INFINITY ? 0.0f : m_run;
     f32x16_t S[2];
 #pragma unroll
     for (int be = 0; be < 2; ++be)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) S[be][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) S[be][i] = -mb;
     bf16x8_t ka[2][8];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
@@ -315,8 +342,7 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
     });
 
     // ---- softmax update for this lane's row.  The maximum is taken on raw
-    // scores (the scale is positive) and the scale is folded into the
-    // exponent: p = 2^(s * scale_log2 - m).
+    // scores, already scaled to log2 units and shifted by -mb: p = 2^(S).
     const int kb = k_lo + (t_begin + t) * kBlkTile;
     const bool edge = (kb + kBlkTile - 1 > i_first) ||
                       (LOCAL && kb <= i_last - kW);
@@ -338,7 +364,7 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
     for (int be = 0; be < 2; ++be)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, S[be][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.scale_log2;
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) + mb;  // tile max, log2 units
     if (__any(mt > m_run + kTauB)) {
       const float mn = fmaxf(m_run, mt);
       const float alpha = mn == m_run ? 1.0f : fast_exp2(m_run - mn);
@@ -348,10 +374,13 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
+      // re-base this tile's scores on the new maximum
+      const float shift = mb - (mn == -INFINITY ? 0.0f : mn);
+#pragma unroll
+      for (int be = 0; be < 2; ++be)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[be][i] += shift;
     }
-    // a row that has seen no visible key yet keeps m = -inf; any finite
-    // base then turns its -inf scores into zero weights
-    const float mb = m_run == -INFINITY ? 0.0f : m_run;
     bf16x8_t P[4];  // 16-key contraction steps: (block be, half tt)
 #pragma unroll
     for (int be = 0; be < 2; ++be)
@@ -360,10 +389,8 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
         uint32_t w4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 =
-              fast_exp2(fmaf(S[be][8 * tt + 2 * j], p.scale_log2, -mb));
-          const float p1 =
-              fast_exp2(fmaf(S[be][8 * tt + 2 * j + 1], p.scale_log2, -mb));
+          const float p0 = fast_exp2(S[be][8 * tt + 2 * j]);
+          const float p1 = fast_exp2(S[be][8 * tt + 2 * j + 1]);
           w4[j] = pack_bf16(p0, p1);
           // the denominator sums exactly the bf16 weights P.V uses
           l_run = dot2_bf16(w4[j], 0x3F803F80u, l_run);
