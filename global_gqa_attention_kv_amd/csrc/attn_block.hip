@@ -285,6 +285,9 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[d][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
+  f32x16_t negmb;  // -(score base) of this lane's row, in all 16 entries
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negmb[i] = 0.0f;
 
   auto consume = [&](int t, auto SLOT) {
     constexpr uint32_t so = SLOT * kSlotB;
@@ -292,29 +295,24 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
     // all requested before its first product and those of block 1 while
     // block 0 multiplies, so no product waits on a fresh LDS read.
     // The accumulators start at -mb (mb: the row's running maximum, 0 while
-    // it has none), so they end up holding s - mb in log2 units.
-    // a row that has seen no visible key yet keeps m = -inf; any finite
-    // base then turns its -inf scores into zero weights
-    const float mb = m_run == -INFINITY ? 0.0f : m_run;
+    // it has none; the first product of each block adds onto the constant
+    // vector negmb), so they end up holding s - mb in log2 units.
+    const float mb = -negmb[0];
     f32x16_t S[2];
-#pragma unroll
-    for (int be = 0; be < 2; ++be)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) S[be][i] = -mb;
     bf16x8_t ka[2][8];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       ka[0][k] = *reinterpret_cast<const lds_bf16x8_t*>(krd[k] + so);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][k], qreg[k], S[0],
-                                                     0, 0, 0);
+      S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          ka[0][k], qreg[k], k == 0 ? negmb : S[0], 0, 0, 0);
       ka[1][k] = *reinterpret_cast<const lds_bf16x8_t*>(krd[k] + so + 8192);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][k], qreg[k], S[1],
-                                                     0, 0, 0);
+      S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          ka[1][k], qreg[k], k == 0 ? negmb : S[1], 0, 0, 0);
     // The V^T operands of the first 16-key step of P.V are requested
     // meanwhile (they do not depend on the softmax).
     constexpr uint32_t vo = so;  // vrd[] already points into the V tile
@@ -374,12 +372,17 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
-      // re-base this tile's scores on the new maximum
-      const float shift = mb - (mn == -INFINITY ? 0.0f : mn);
+      // re-base this tile's scores (and the next tiles') on the new maximum;
+      // a row that has seen no visible key yet keeps m = -inf and base 0,
+      // which turns its -inf scores into zero weights
+      const float nb = mn == -INFINITY ? 0.0f : mn;
+      const float shift = mb - nb;
 #pragma unroll
       for (int be = 0; be < 2; ++be)
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[be][i] += shift;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negmb[i] = -nb;
     }
     bf16x8_t P[4];  // 16-key contraction steps: (block be, half tt)
 #pragma unroll
