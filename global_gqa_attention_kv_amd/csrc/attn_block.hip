@@ -79,6 +79,20 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
       : "v"(src), "s"(lds)
       : "memory");
 }
+// The same from a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16(const uint16_t* base, uint32_t off,
+                                      uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
 __device__ __forceinline__ void wait_vmcnt0() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -248,16 +262,56 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   const int rsub = lane >> 4, cs = lane & 15;
   auto vswz = [](int r) { return 4 * (r & 3) + 2 * ((r >> 1) & 1); };
+  // byte offsets of this lane's chunks from the tile's first key row
+  uint32_t kdma[LPT], vdma[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int r = RPW * w + 4 * i + rsub;
+    kdma[i] = r * (kTokenElems * 2) + ((cs ^ (r & 15)) << 4);
+    vdma[i] = r * (kTokenElems * 2) + ((cs ^ vswz(r)) << 4);
+  }
   auto issue_tile = [&](int t, auto SLOT) {
     const int kb = k_lo + (t_begin + t) * kBlkTile;
     const uint32_t kl = __builtin_amdgcn_readfirstlane(
         lds_base + SLOT * kSlotB + w * RPW * 256);
+    // A full tile whose rows are consecutive in one buffer loads from a
+    // wave-uniform base; otherwise (range end, cache/block boundary, ring
+    // wrap) each row is located on its own.
+    const bool full = kb + kBlkTile <= k_hi;
+    const bool in_cache = kb + kBlkTile <= pos0, in_blk = kb >= pos0;
+    const int ring = LOCAL ? (kb & (kW - 1)) : kb;
+    const uint16_t* kt =
+        !full ? nullptr
+        : LOCAL ? kl_base + (kb - klin0) * kTokenElems
+        : in_cache ? kc_base + kb * kTokenElems
+        : in_blk ? kb_base + (kb - pos0) * kTokenElems : nullptr;
+    const uint16_t* vt =
+        !full ? nullptr
+        : in_cache ? (!LOCAL || ring + kBlkTile <= kW
+                          ? vc_base + ring * kTokenElems : nullptr)
+        : in_blk ? vb_base + (kb - pos0) * kTokenElems : nullptr;
+    if (kt) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int r = RPW * w + 4 * i + rsub;
-      const int j = min(kb + r, k_hi - 1);
-      dma16(k_src(j) + ((cs ^ (r & 15)) << 3), kl + i * 1024);
-      dma16(v_src(j) + ((cs ^ vswz(r)) << 3), kl + kTileB + i * 1024);
+      for (int i = 0; i < LPT; ++i) dma16(kt, kdma[i], kl + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int r = RPW * w + 4 * i + rsub;
+        dma16(k_src(min(kb + r, k_hi - 1)) + ((cs ^ (r & 15)) << 3),
+              kl + i * 1024);
+      }
+    }
+    if (vt) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i)
+        dma16(vt, vdma[i], kl + kTileB + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int r = RPW * w + 4 * i + rsub;
+        dma16(v_src(min(kb + r, k_hi - 1)) + ((cs ^ vswz(r)) << 3),
+              kl + kTileB + i * 1024);
+      }
     }
   };
 
