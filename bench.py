@@ -89,7 +89,7 @@ def build_decode_step(ga, torch, B, pos, seed=1003):
                                  device=dev).to(torch.bfloat16))
         vnews.append(torch.randn((B, 1, ga.HKV, ga.D), generator=gen,
                                  device=dev).to(torch.bfloat16))
-    ws = torch.zeros(max(ga.workspace_bytes(ga.OP_DECODE, k, B, 1, CTX)
+    ws = torch.empty(max(ga.workspace_bytes(ga.OP_DECODE, k, B, 1, CTX)
                          for k in (ga.LOCAL, ga.GLOBAL)),
                      dtype=torch.uint8, device=dev)
     outs = [torch.empty((B, ga.HQ, ga.D), dtype=torch.float32, device=dev)
@@ -112,6 +112,19 @@ def build_decode_step(ga, torch, B, pos, seed=1003):
     step.local_only = step_kind(ga.LOCAL)
     step.global_only = step_kind(ga.GLOBAL)
     return kinds, layers, qs, outs, ws, positions, step
+
+
+def check_step_outputs(ga, torch, layers, qs, outs, positions, kinds):
+    """The replayed step shares one workspace across all 52 layers; a
+    local and a global layer's outputs must equal a fresh eager call's with
+    a workspace of its own (same kernels, same merge order: bit-identical)."""
+    for l in (kinds.index(ga.LOCAL), kinds.index(ga.GLOBAL)):
+        again = ga.attn_decode(layers[l], qs[l], positions)
+        torch.cuda.synchronize()
+        diff = (again - outs[l]).abs().max().item()
+        if not diff <= 1e-6:
+            raise RuntimeError("decode step output of layer %d differs from "
+                               "an eager call by %g" % (l, diff))
 
 
 def time_graph(torch, fn, steps, warmup):
@@ -350,6 +363,7 @@ def main():
           file=sys.stderr, flush=True)
 
     ms, _graph = time_graph(torch, step, args.steps, args.warmup)
+    check_step_outputs(ga, torch, layers, qs, outs, positions, kinds)
     kvb = kv_bytes_step(kinds, positions)
     value = kvb / (ms * 1e-3) / 1e9
 

@@ -192,11 +192,13 @@ def kv_append(layer: Layer, k_new, v_new, pos0, stream=None):
 
 
 def workspace(op, kind, B, n, max_ctx, device="cuda"):
-    """A zero-filled workspace tensor for the given operation and shape."""
+    """A workspace tensor for the given operation and shape (no
+    initialisation needed; one tensor may serve every operation issued in
+    order on a stream)."""
     need = workspace_bytes(op, kind, B, n, max_ctx)
     if need == 0:
         raise ValueError("invalid workspace request")
-    return torch.zeros(need, dtype=torch.uint8, device=device)
+    return torch.empty(need, dtype=torch.uint8, device=device)
 
 
 def _decode_common(fn, name, layer, q, pos, out, ws, stream, extra=()):
@@ -221,7 +223,7 @@ def _decode_common(fn, name, layer, q, pos, out, ws, stream, extra=()):
 
 def attn_decode(layer: Layer, q, pos, out=None, ws=None, stream=None):
     """One decode step.  q: bf16 [B, 32, 128]; pos: B host positions of the
-    query tokens (already appended).  ws: zero-filled workspace (see
+    query tokens (already appended).  ws: workspace (see
     :func:`workspace`), allocated per call when omitted.
     Returns out: fp32 [B, 32, 128]."""
     return _decode_common(_load().gqa_attn_decode, "gqa_attn_decode", layer,

@@ -16,7 +16,8 @@ namespace {
 // Global-layer decode: as many wide-kernel workgroups as fit the 256 CUs at
 // once, so the launch runs as one full round (a partial second round would
 // leave part of the device idle at the end).
-constexpr int kDecodeTargetWGs = 256 * kWideWGsPerCU;
+constexpr int kDecodeTargetWGs = 256 * kGlobalWGsPerCU;
+static_assert(kDecodeTargetWGs / 2 <= kMaxSplits, "merge kernel capacity");
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
@@ -24,19 +25,15 @@ DecodePlan plan_decode(int kind, int B, int64_t max_keys) {
   const int64_t tiles = (max_keys + kDecTile - 1) / kDecTile;
   DecodePlan p;
   if (kind == GQA_LOCAL) {
-    p.narrow = true;
-    p.heads_per_wg = 4;
-    p.head_groups = kGroup / 4;
-    // one tile per workgroup for a single sequence (latency-bound); two
-    // for larger batches so every workgroup of the launch is resident at once
-    p.tiles_per_split = B >= 2 ? 2 : 1;
+    // the window is 32 tiles: one tile per workgroup up to batch 4 (256
+    // workgroups), then longer splits so a launch stays near 256
+    p.tiles_per_split = B >= 8 ? B / 4 : 1;
+    if (p.tiles_per_split > (int)tiles) p.tiles_per_split = (int)tiles;
+    if (p.tiles_per_split < 1) p.tiles_per_split = 1;
     p.splits = (int)((tiles + p.tiles_per_split - 1) / p.tiles_per_split);
     if (p.splits < 1) p.splits = 1;
     return p;
   }
-  p.narrow = false;
-  p.heads_per_wg = kGroup;
-  p.head_groups = 1;
   int64_t want = kDecodeTargetWGs / (2 * B);
   if (want < 1) want = 1;
   int64_t per = (tiles + want - 1) / want;
@@ -47,12 +44,10 @@ DecodePlan plan_decode(int kind, int B, int64_t max_keys) {
   return p;
 }
 
-// Workspace: partial sums [B][2][head_groups][splits][heads_per_wg x 130]
-// floats, then one int32 counter per (sequence, KV head, head group).
+// Workspace: the partial sums [B][2][splits][16 x 130] floats.
 size_t decode_ws_bytes(int B, const DecodePlan& plan) {
-  const size_t parts = (size_t)B * kHkv * plan.head_groups * plan.splits *
-                       part_floats(plan) * sizeof(float);
-  return align256(parts) + align256((size_t)B * kHkv * plan.head_groups * 4);
+  return align256((size_t)B * kHkv * plan.splits * kPartFloats *
+                  sizeof(float));
 }
 
 // Block operations.  Verification (<= 16 tokens) uses 16-token workgroups
@@ -91,6 +86,7 @@ BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify) {
   return p;
 }
 
+// Rotated keys (local layers), then partial sums (split keys).
 size_t block_ws_bytes(const BlockPlan& plan) {
   const size_t n = plan.klin_bytes + plan.part_bytes;
   return n ? n : 256;
@@ -172,6 +168,7 @@ static int decode_impl(const gqa_layer* layer, const void* q,
       return GQA_ERR_MISALIGNED;
   }
   const DecodePlan plan = plan_decode(layer->kind, B, max_keys);
+  if (plan.splits > kMaxSplits) return GQA_ERR_UNSUPPORTED;
   const size_t need = decode_ws_bytes(B, plan);
   if (!ws) return GQA_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
@@ -185,11 +182,7 @@ static int decode_impl(const gqa_layer* layer, const void* q,
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
   p.q = static_cast<const uint32_t*>(q);
-  const size_t parts = (size_t)B * kHkv * plan.head_groups * plan.splits *
-                       part_floats(plan) * sizeof(float);
   p.part = static_cast<float*>(ws);
-  p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
-                                          align256(parts));
   p.out = out;
   p.seq_stride = layer->seq_stride;
   p.scale_log2 = (float)(1.0 / sqrt((double)kD) * 1.4426950408889634);
@@ -244,10 +237,11 @@ static int block_impl(const gqa_layer* layer, const void* q,
   p.v_blk = static_cast<const uint16_t*>(v_blk);
   p.k_cache = static_cast<const uint16_t*>(layer->k);
   p.v_cache = static_cast<const uint16_t*>(layer->v);
-  p.k_lin = plan.klin_bytes ? static_cast<uint16_t*>(ws) : nullptr;
-  p.part = plan.part_bytes ? reinterpret_cast<float*>(
-                                 static_cast<char*>(ws) + plan.klin_bytes)
-                           : nullptr;
+  char* const scratch = static_cast<char*>(ws);
+  p.k_lin = plan.klin_bytes ? reinterpret_cast<uint16_t*>(scratch) : nullptr;
+  p.part = plan.part_bytes
+               ? reinterpret_cast<float*>(scratch + plan.klin_bytes)
+               : nullptr;
   p.out = out;
   p.seq_stride = layer->seq_stride;
   p.klin_rows = (int64_t)kW + n;

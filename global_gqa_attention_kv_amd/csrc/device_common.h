@@ -44,6 +44,18 @@ __device__ __forceinline__ float dot2_bf16_bcast(uint32_t q, uint32_t k,
   return acc;
 }
 
+// The result of a DPP product is not ready for a plain VALU read two wait
+// states later (measured: the last product of a chain was lost when its
+// accumulator was summed that soon).  A chain of products updates each
+// accumulator four instructions apart, which holds; after the chain's last
+// product, this puts five wait states before any other use of the four
+// accumulators.  The operands tie the wait to them, so the compiler cannot
+// move their readers above it.  A host test checks the generated code.
+__device__ __forceinline__ void dpp_settle(float& a, float& b, float& c,
+                                           float& d) {
+  asm volatile("s_nop 4" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
 // Calls f(I) for I = 0 .. N-1 with I a compile-time constant.
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -70,14 +82,6 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// Interleave the bf16 lanes of two words: (a.lo, b.lo) and (a.hi, b.hi).
-__device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
@@ -87,25 +91,6 @@ __device__ __forceinline__ float fast_exp2(float x) {
 __device__ __forceinline__ void sincos_rev(float r, float* s, float* c) {
   *s = __builtin_amdgcn_sinf(r);
   *c = __builtin_amdgcn_cosf(r);
-}
-
-// Device-scope (all XCDs) coherent store and load of one word: the store is
-// written through to the coherence point instead of staying dirty in this
-// XCD's L2, and the load does not trust a stale L2 copy.  With these, a
-// workgroup can hand data to a workgroup on another XCD inside one launch
-// with only a store-completion wait before a device-scope counter update,
-// instead of a full L2 write-back fence.
-__device__ __forceinline__ void store_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-}
-// s_waitcnt vmcnt(0): every vector memory operation of this wave has
-// completed (stores acknowledged at their scope).
-__device__ __forceinline__ void wait_vmem() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 // RoPE on bf16 data: rotate the pairs (lo[i], hi[i]) -- dims d and d + 64
@@ -124,16 +109,6 @@ __device__ __forceinline__ void rope_pair(uint32_t& lo, uint32_t& hi,
   sincos_rev(r1, &s1, &c1);
   lo = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
   hi = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
-}
-
-// Rotate the 8 dims held in lo (dims d..d+7) against their partners in hi
-// (dims d+64..d+71); rev points at the 8 frequencies of dims d..d+7.
-__device__ __forceinline__ void rope_rotate(uint4& lo, uint4& hi, float delta,
-                                            const float* rev) {
-  rope_pair(lo.x, hi.x, delta, rev[0], rev[1]);
-  rope_pair(lo.y, hi.y, delta, rev[2], rev[3]);
-  rope_pair(lo.z, hi.z, delta, rev[4], rev[5]);
-  rope_pair(lo.w, hi.w, delta, rev[6], rev[7]);
 }
 
 __device__ __forceinline__ float wave_max(float x) {

@@ -36,37 +36,29 @@ hipError_t launch_kv_append(const AppendParams& p, int B, int count,
 
 // ---------------------------------------------------------------- decode
 constexpr int kDecTile = 64;               // keys per tile
-constexpr int kDecThreads = 256;           // 4 waves
-// Global-layer (wide) decode kernel: waves per workgroup (16 / waves query
-// heads each), tile slots in its LDS ring (32 KB each), and how many such
-// workgroups fit one CU.  Four waves with a two-slot ring, two workgroups
-// per CU, measured fastest: eight waves (two heads each) or a single
-// workgroup with a deeper ring lose more VALU efficiency than they gain in
-// loads in flight.
-constexpr int kWideWaves = 4;
-constexpr int kWideRing = 2;
-constexpr int kWideWGsPerCU = kWideRing <= 2 ? 2 : 1;
+// Global-layer decode: waves per workgroup (16 / waves query heads each),
+// tile slots in its LDS ring (32 KB each), and how many such workgroups fit
+// one CU.  Four waves with a two-slot ring, two workgroups per CU, measured
+// fastest: eight waves (two heads each) or a single workgroup with a deeper
+// ring lose more VALU efficiency than they gain in loads in flight.
+constexpr int kGlobalWaves = 4;
+constexpr int kGlobalRing = 2;
+constexpr int kGlobalWGsPerCU = kGlobalRing <= 2 ? 2 : 1;
+// Local-layer decode (latency-bound, one tile per workgroup): 8 waves of 2
+// heads put more waves behind each tile than 4 waves of 4 heads.
+constexpr int kLocalWaves = 8;
+// Most key splits of one decode call (the merge kernel loads them all at once).
+constexpr int kMaxSplits = 256;
 
-// Two launch shapes:
-//  * wide (decode_wide_kernel): a workgroup serves all 16 query heads of its
-//    KV head and a long key split; a separate kernel merges the splits.
-//    Used where the cache is large (global layers).
-//  * narrow (decode_kernel): a workgroup serves 4 query heads (1 per wave)
-//    and one or two tiles; the four head groups of one tile run on the same
-//    XCD so three of them hit L2, and the last workgroup of each (sequence,
-//    KV head, head group) merges the splits in the same launch.  Used for
-//    the 2048-key local windows, where latency rather than bandwidth sets
-//    the time.
+// A workgroup serves all 16 query heads of one (sequence, KV head) over a
+// split of tiles_per_split tiles; a second kernel merges the splits.
 struct DecodePlan {
-  bool narrow;
-  int heads_per_wg;     // 16 (wide) or 4 (narrow)
-  int head_groups;      // 16 / heads_per_wg
   int splits;           // S: key splits per (sequence, KV head)
   int tiles_per_split;  // tiles of kDecTile keys per split
 };
 DecodePlan plan_decode(int kind, int B, int64_t max_keys);
 size_t decode_ws_bytes(int B, const DecodePlan& plan);
-inline int part_floats(const DecodePlan& pl) { return pl.heads_per_wg * (kD + 2); }
+constexpr int kPartFloats = kGroup * (kD + 2);  // m[16], l[16], o[16][128]
 
 struct DecodeParams {
   const uint16_t* k;       // cache base (sequence 0, slot 0, head 0)
@@ -77,7 +69,6 @@ struct DecodeParams {
   const uint16_t* v_new;
   const uint32_t* q;       // [B][32][64] bf16 pairs
   float* part;             // partial sums, see decode.hip
-  int32_t* counters;       // [B][2][head_groups], zero between calls
   float* out;              // [B][32][128]
   int64_t seq_stride;      // elements
   float scale_log2;        // softmax scale * log2(e)

@@ -29,6 +29,13 @@
  *     reports a failed launch).  Faults inside a kernel surface at the
  *     caller's next synchronisation.  No C++ exception crosses the ABI.
  *   - Batch size B is 1 .. GQA_MAX_BATCH.
+ *   - Workspaces: every attention call takes a caller-owned scratch buffer
+ *     `ws` (256-byte aligned) of at least gqa_workspace_bytes(op, ...) bytes
+ *     for its partial results.  It needs no initialisation and carries
+ *     nothing from one call to the next, so one workspace, sized for the
+ *     largest request, serves every operation and layer kind issued in order
+ *     on one stream.  Calls that may overlap in time need separate
+ *     workspaces.
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -104,12 +111,8 @@ int gqa_kv_append(const gqa_layer* layer, const void* k_new, const void* v_new,
  * local layers to max(0, pos[b]-2047)..pos[b] through the ring, with RoPE.
  * Scale 1/sqrt(128).  The key range is split across workgroups (split-K)
  * whose partial softmax sums are merged on the device.
- * Workspace: `ws` (256-byte aligned) must hold
- * gqa_workspace_bytes(GQA_OP_DECODE, kind, B, 1, max pos + 1) bytes and be
- * zero-filled once before its first use; every call leaves it zero-filled
- * again (it holds split counters), so one workspace serves any number of
- * calls issued in order on one stream.  Calls that may overlap in time need
- * separate workspaces.
+ * Workspace: gqa_workspace_bytes(GQA_OP_DECODE, kind, B, 1, max pos + 1)
+ * bytes (see the workspace rules above).
  * Pages: shishifenxi.com section 01 (each new token reads the cached keys
  * and values); runtimewire.com "Narrow cache" and "Long context still costs
  * compute". */
@@ -136,8 +139,8 @@ int gqa_attn_decode_append(const gqa_layer* layer, const void* q,
  * block).  The call does not touch the cache: append the accepted prefix
  * afterwards with gqa_kv_append, so rejected drafts never overwrite ring
  * entries that are still inside the window.  Global layers need
- * pos0[b] + n <= capacity.  ws (256-byte aligned, no initialisation) must
- * hold gqa_workspace_bytes(GQA_OP_VERIFY, kind, B, n, max pos0 + n) bytes.
+ * pos0[b] + n <= capacity.  ws must hold
+ * gqa_workspace_bytes(GQA_OP_VERIFY, kind, B, n, max pos0 + n) bytes.
  * Pages: shishifenxi.com section 04 (a block of 16 drafted tokens verified
  * by the main model at once); kongchang.com "Meta open-sources the 30B Muse
  * Glimmer", "Trick 3: D-Flash" (parallel verification under the causal
@@ -150,9 +153,9 @@ int gqa_attn_verify(const gqa_layer* layer, const void* q, const void* k_blk,
  * positions pos0[b] .. pos0[b]+n-1.  Same visibility rules and arguments as
  * gqa_attn_verify (the chunk's K/V are passed in and not appended; the
  * cache holds the positions before pos0[b]), but out is bf16 [B][n][32][128],
- * rounded to nearest even from fp32.  ws (256-byte aligned, no
- * initialisation) must hold gqa_workspace_bytes(GQA_OP_PREFILL, kind, B, n,
- * max pos0 + n) bytes.  Append the chunk with gqa_kv_append afterwards.
+ * rounded to nearest even from fp32.  ws must hold
+ * gqa_workspace_bytes(GQA_OP_PREFILL, kind, B, n, max pos0 + n) bytes.
+ * Append the chunk with gqa_kv_append afterwards.
  * Pages: runtimewire.com "Long context still costs compute" (global layers
  * run full attention during prompt processing with memory-efficient kernels
  * that never store the attention matrix; the cost stays quadratic). */

@@ -2,11 +2,16 @@
 
 The query-key products are written as inline assembly (v_dot2c_f32_bf16 with
 a DPP row broadcast), which the compiler's hazard recognizer cannot see
-through.  The hardware requires two wait states between a VALU write of a
-VGPR and a DPP instruction reading it.  This test compiles decode.hip to
-assembly (no GPU needed) and checks every DPP product: none of its VGPR
-operands may have been written by a VALU instruction less than two wait
-states earlier in the same basic block."""
+through.  Two rules are checked on the assembly of decode.hip (no GPU
+needed), within each basic block:
+  * the hardware requires two wait states between a VALU write of a VGPR
+    and a DPP instruction reading it: none of a DPP product's VGPR operands
+    may have been written by a VALU instruction less than two wait states
+    earlier;
+  * a DPP product's result needs more time before a plain read: an
+    instruction other than a further product into the same accumulator may
+    read it only four or more wait states later (two were measured to lose
+    the product)."""
 import os
 import re
 import shutil
@@ -81,4 +86,57 @@ def test_dpp_products_respect_wait_states():
             else:
                 waits += 1
             j -= 1
+    assert n_dpp > 0, "no DPP products found: did the kernel change?"
+
+
+def _reads(insn):
+    """VGPRs an instruction reads (for VALU: every operand but the
+    destination, plus the destination of accumulating forms)."""
+    parts = insn.split(None, 1)
+    if len(parts) < 2:
+        return set()
+    op, rest = parts
+    ops = [o.strip() for o in rest.split(",")]
+    regs = set()
+    start = 1 if op.startswith("v_") else 0
+    if op.startswith("v_") and ("dot2c" in op or "fmac" in op or "mac_" in op):
+        start = 0
+    if op.startswith(("global_store", "buffer_store", "ds_write", "ds_store")):
+        start = 0
+    for o in ops[start:]:
+        regs |= _regs(o.split()[0] if o else o)
+    return regs
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="needs hipcc")
+def test_dpp_results_settle_before_plain_reads():
+    text = _assemble(os.path.join(CSRC, "decode.hip"))
+    lines = []
+    for raw in text.splitlines():
+        l = raw.strip()
+        if not l or l.startswith(";") or l.startswith("."):
+            continue
+        lines.append(("LABEL", l) if l.endswith(":") else ("INSN", l))
+    n_dpp = 0
+    for i, (kind, l) in enumerate(lines):
+        if kind != "INSN" or not l.startswith("v_dot2c_f32_bf16_dpp"):
+            continue
+        n_dpp += 1
+        dst = _regs(l.split(None, 1)[1].split(",")[0])
+        waits = 0
+        j = i + 1
+        while j < len(lines) and waits < 4:
+            k2, nxt = lines[j]
+            if k2 == "LABEL" or nxt.startswith("s_cbranch") or \
+                    nxt.startswith("s_branch"):
+                break
+            op = nxt.split()[0]
+            if op.startswith("v_dot2c_f32_bf16_dpp") and \
+                    _regs(nxt.split(None, 1)[1].split(",")[0]) == dst:
+                break  # the chain goes on into the same accumulator
+            assert not (_reads(nxt) & dst), (
+                "DPP result read too early: '%s' then '%s' after %d wait "
+                "states" % (l, nxt, waits))
+            waits += int(nxt.split()[1], 0) + 1 if op == "s_nop" else 1
+            j += 1
     assert n_dpp > 0, "no DPP products found: did the kernel change?"
