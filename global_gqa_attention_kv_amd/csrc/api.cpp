@@ -60,7 +60,7 @@ constexpr int kBlockTargetWGs = 256;
 
 BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify) {
   BlockPlan p;
-  p.qpw = 16;
+  p.qpw = kBlkQpw;
   p.qgroups = (n + p.qpw - 1) / p.qpw;
   // keys one workgroup may see: its window (local) or everything before it
   const int64_t wg_keys =

@@ -15,20 +15,19 @@
 // block verified by the main model in one pass, causal within the block).
 //
 // Design (gfx950, v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//  * Rows are (query, head) pairs: a workgroup takes QPW query tokens x the
-//    16 query heads of one KV head, so every K/V tile staged in LDS serves
-//    16 x QPW rows (GQA reuse); each wave owns 32 rows = 2 tokens x 16 heads.
+//  * Rows are (query, head) pairs: a workgroup takes 16 query tokens x the
+//    16 query heads of one KV head (256 rows, 8 waves of 32 rows = 2 tokens
+//    x 16 heads), so every K/V tile staged in LDS serves 256 rows (GQA
+//    reuse).  8 waves (two per SIMD) and 224 VGPRs each: one workgroup per
+//    CU.
 //  * Scores are formed transposed, S^T = K Q^T, so each lane ends up owning
 //    one row and 16 keys of every 32-key block: the row maximum is 31 in-lane
 //    max operations plus one exchange with the partner lane 32 away, and the
 //    probabilities, rounded to bf16, are directly the B operand of the P.V
-//    product (O^T = V^T P^T) -- P never goes through LDS.  The contraction's
-//    key order inside each 16-key step follows the score layout; V^T is read
-//    in that same order.
-//  * K tiles sit in LDS row-major (rows padded to 272 B); V tiles are
-//    transposed on their way into LDS (rows of 64 keys padded to 136 B, the
-//    8-byte units XOR-swizzled by dim/8 against write conflicts) so a lane
-//    reads 4 consecutive keys of one dimension with one 8-byte load.
+//    product (O^T = V^T P^T) -- P never goes through LDS.
+//  * Tiles of 64 keys stream into a four-slot LDS ring with direct-to-LDS
+//    loads (no VGPR staging).  Rows of 256 bytes (one key), 16-byte chunks
+//    XOR-swizzled per row; the V^T operand is read with ds_read_b64_tr_b16.
 //  * Online softmax in the log2 domain with a lazy maximum (rescale only when
 //    a score exceeds the running maximum by more than 2^8); masks are applied
 //    only on tiles that cross the causal diagonal or the window edge.
@@ -54,8 +53,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kTauB = 8.0f;
 constexpr int kTileB = kBlkTile * 256;      // one 64-key tile of K or V
 constexpr int kSlotB = 2 * kTileB;          // K tile, then V tile
-template <int QPW>
-constexpr int kBlockRing = QPW == 16 ? 4 : 2;  // tile slots in LDS
+constexpr int kRing = 4;                    // tile slots in LDS (128 KB)
+constexpr int kWaves = kBlkQpw / 2;         // 8 waves of 32 rows
 constexpr int kPartRow = 132;               // floats: o[128], m, l, pad
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -132,25 +131,19 @@ __global__ __launch_bounds__(64) void rope_keys_kernel(const BlockParams p) {
   d32[c + 32] = y;
 }
 
-// QPW = 8: 256 threads, a two-slot ring, two workgroups per CU (64 KB of
-// LDS each).  QPW = 16: 512 threads (two waves per SIMD from one
-// workgroup) sharing each tile among twice the rows, so a CU needs half the
-// tile traffic, with a three-slot ring (96 KB) that loads two tiles ahead.
-//
-// Tiles stream into a two-slot LDS ring with direct-to-LDS loads: tile t + 1
-// is in flight while tile t is consumed, and no VGPRs or VALU work stage
-// it.  Both tiles keep rows of 256 bytes (one key), their 16-byte chunks
-// XOR-swizzled per row: K chunk c of row r at slot c ^ (r & 15), so the 32
-// lanes reading one chunk of 32 consecutive keys hit distinct banks; V chunk
-// c at slot c ^ X(r & 3), X = {0, 4, 10, 14}.  The V^T operand of the P.V
-// product is read with ds_read_b64_tr_b16, which returns four consecutive
-// keys of one dimension per lane; X puts the four keys of a 16-lane group,
-// and the 64 bytes of each key read by a 32-lane half, on distinct banks.
-template <int QPW, bool LOCAL, bool SPLIT, bool OUT_F32>
-__global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
+// Tile t goes to ring slot t % 4, loaded three tiles ahead (direct-to-LDS,
+// so tile t + 3 is in flight while tile t is consumed).  K chunk c of row r
+// sits at chunk
+// slot c ^ (r & 15), so the 32 lanes reading one chunk of 32 consecutive
+// keys hit distinct banks; V chunk c at slot c ^ X(r & 3), X = {0, 4, 10,
+// 14}: the four keys of a 16-lane group of ds_read_b64_tr_b16, and the 64
+// bytes of each key read by a 32-lane half, land on distinct banks.
+template <bool LOCAL, bool SPLIT, bool OUT_F32>
+__global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
     const BlockParams p) {
-  constexpr int WAVES = QPW / 2;
-  constexpr int RING = kBlockRing<QPW>;
+  constexpr int QPW = kBlkQpw;
+  constexpr int WAVES = kWaves;
+  constexpr int RING = kRing;
   constexpr int ROWS = QPW * kGroup;
   constexpr int RPW = kBlkTile / WAVES;   // tile rows each wave loads
   constexpr int LPT = RPW / 4;            // 1-KB loads per K or V tile per wave
@@ -548,10 +541,14 @@ __global__ __launch_bounds__(QPW * 32, 16 / QPW) void block_attn_kernel(
 }
 
 // Merge the key splits of one (sequence, token, query head, quarter of the
-// head dimension): 8 float4 columns x 32 split lanes per workgroup.
-template <int QPW, bool OUT_F32>
+// head dimension): 32 split lanes x 8 float4 columns per workgroup (thread =
+// 8 lane + column), every split's loads in flight at once.  The largest split
+// maximum M is found first, so the weighted sums need no rescaling and the
+// split lanes combine by plain addition:
+// o = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s.
+template <bool OUT_F32>
 __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
-  constexpr int ROWS = QPW * kGroup;
+  constexpr int ROWS = kBlkQpw * kGroup;
   const int dq = blockIdx.x & 3;
   int rest = blockIdx.x >> 2;
   const int h = rest % kHq;
@@ -559,88 +556,98 @@ __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
   const int qi = rest % p.n;
   const int b = rest / p.n;
   const int g = h / kGroup;
-  const int qg = qi / QPW;
-  const int prow = (qi - qg * QPW) * kGroup + (h % kGroup);
+  const int qg = qi / kBlkQpw;
+  const int prow = (qi - qg * kBlkQpw) * kGroup + (h % kGroup);
   const float* base =
       p.part + (((size_t)(b * kHkv + g) * p.qgroups + qg) * p.splits * ROWS +
                 prow) * kPartRow;
-  const size_t sstride = (size_t)ROWS * kPartRow;
+  constexpr size_t sstride = (size_t)ROWS * kPartRow;
   const int tid = threadIdx.x;
-  const int c4 = tid & 7, sl = tid >> 3;
+  const int c4 = tid & 7, sl = tid >> 3, w = tid >> 6;
   const int d = dq * 32 + c4 * 4;
-  float M = -INFINITY, L = 0.0f;
-  float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  constexpr int kBatch = 4;
-  for (int s0 = sl; s0 < p.splits; s0 += 32 * kBatch) {
-    float ms[kBatch], ls[kBatch];
-    float4 os[kBatch];
+  __shared__ float wmax[4];
+  __shared__ float4 wsum[4][8];
+  __shared__ float wl[4][8];
+  constexpr int kPer = kMaxSplits / 32;  // the planner keeps splits <= 256
+  float ms[kPer], ls[kPer];
+  float4 os[kPer];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int s = s0 + 32 * i;
-      const float* ps = base + (size_t)min(s, p.splits - 1) * sstride;
-      ms[i] = s < p.splits ? ps[kD] : -INFINITY;
-      ls[i] = ps[kD + 1];
-      os[i] = *reinterpret_cast<const float4*>(ps + d);
-    }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (ms[i] == -INFINITY) continue;
-      const float mn = fmaxf(M, ms[i]);
-      const float a = fast_exp2(M - mn), c = fast_exp2(ms[i] - mn);
-      L = L * a + ls[i] * c;
-      O.x = O.x * a + os[i].x * c;
-      O.y = O.y * a + os[i].y * c;
-      O.z = O.z * a + os[i].z * c;
-      O.w = O.w * a + os[i].w * c;
-      M = mn;
-    }
+  for (int i = 0; i < kPer; ++i) {
+    const int s = sl + 32 * i;
+    const float* ps = base + (size_t)min(s, p.splits - 1) * sstride;
+    ms[i] = s < p.splits ? ps[kD] : -INFINITY;
+    ls[i] = ps[kD + 1];
+    os[i] = *reinterpret_cast<const float4*>(ps + d);
   }
-  __shared__ float red[32][8][6];
-  red[sl][c4][0] = M;
-  red[sl][c4][1] = L;
-  red[sl][c4][2] = O.x;
-  red[sl][c4][3] = O.y;
-  red[sl][c4][4] = O.z;
-  red[sl][c4][5] = O.w;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) mx = fmaxf(mx, ms[i]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) wmax[w] = mx;
   __syncthreads();
-  if (sl != 0) return;
-  float Mt = -INFINITY;
-  for (int i = 0; i < 32; ++i) Mt = fmaxf(Mt, red[i][c4][0]);
-  float Lt = 0.0f, x = 0.0f, y = 0.0f, z = 0.0f, ww = 0.0f;
-  for (int i = 0; i < 32; ++i) {
-    if (red[i][c4][0] == -INFINITY) continue;
-    const float c = fast_exp2(red[i][c4][0] - Mt);
-    Lt += red[i][c4][1] * c;
-    x += red[i][c4][2] * c;
-    y += red[i][c4][3] * c;
-    z += red[i][c4][4] * c;
-    ww += red[i][c4][5] * c;
+  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  // splits without visible keys (m = -inf) and padding lanes weigh 0
+  float L = 0.0f;
+  float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const float c = fast_exp2(ms[i] - M);
+    L += ls[i] * c;
+    O.x += os[i].x * c;
+    O.y += os[i].y * c;
+    O.z += os[i].z * c;
+    O.w += os[i].w * c;
+  }
+  // the 8 split lanes of a wave that share a column are 8 apart
+#pragma unroll
+  for (int o = 8; o <= 32; o <<= 1) {
+    L += __shfl_xor(L, o, 64);
+    O.x += __shfl_xor(O.x, o, 64);
+    O.y += __shfl_xor(O.y, o, 64);
+    O.z += __shfl_xor(O.z, o, 64);
+    O.w += __shfl_xor(O.w, o, 64);
+  }
+  if ((tid & 63) < 8) {
+    wsum[w][c4] = O;
+    wl[w][c4] = L;
+  }
+  __syncthreads();
+  if (tid >= 8) return;
+  float Lt = 0.0f;
+  float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    Lt += wl[j][c4];
+    r.x += wsum[j][c4].x;
+    r.y += wsum[j][c4].y;
+    r.z += wsum[j][c4].z;
+    r.w += wsum[j][c4].w;
   }
   const float inv = 1.0f / Lt;
   const size_t o = (((size_t)b * p.n + qi) * kHq + h) * kD + d;
   if constexpr (OUT_F32) {
     *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) =
-        make_float4(x * inv, y * inv, z * inv, ww * inv);
+        make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
   } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
-        make_uint2(pack_bf16(x * inv, y * inv), pack_bf16(z * inv, ww * inv));
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(
+        pack_bf16(r.x * inv, r.y * inv), pack_bf16(r.z * inv, r.w * inv));
   }
 }
 
-template <int QPW, bool LOCAL, bool OUT_F32>
+template <bool LOCAL, bool OUT_F32>
 hipError_t launch_main(const BlockParams& p, int B, hipStream_t s) {
   const dim3 grid(p.splits * p.qgroups * kHkv * B);
-  const dim3 block(QPW * 32);
+  const dim3 block(kWaves * 64);
   if (p.splits > 1) {
-    hipLaunchKernelGGL((block_attn_kernel<QPW, LOCAL, true, OUT_F32>), grid,
-                       block, 0, s, p);
+    hipLaunchKernelGGL((block_attn_kernel<LOCAL, true, OUT_F32>), grid, block,
+                       0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((block_merge_kernel<QPW, OUT_F32>),
+    hipLaunchKernelGGL((block_merge_kernel<OUT_F32>),
                        dim3(B * p.n * kHq * 4), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((block_attn_kernel<QPW, LOCAL, false, OUT_F32>), grid,
-                       block, 0, s, p);
+    hipLaunchKernelGGL((block_attn_kernel<LOCAL, false, OUT_F32>), grid, block,
+                       0, s, p);
   }
   return hipGetLastError();
 }
@@ -649,24 +656,17 @@ hipError_t launch_main(const BlockParams& p, int B, hipStream_t s) {
 
 hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
                         bool local, bool out_f32, int B, hipStream_t s) {
+  if (plan.qpw != kBlkQpw || p.splits > kMaxSplits) return hipErrorInvalidValue;
   if (local) {
     hipLaunchKernelGGL(rope_keys_kernel, dim3((unsigned)p.klin_rows, B),
                        dim3(64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return out_f32 ? launch_main<true, true>(p, B, s)
+                   : launch_main<true, false>(p, B, s);
   }
-  if (plan.qpw == 16) {
-    if (local)
-      return out_f32 ? launch_main<16, true, true>(p, B, s)
-                     : launch_main<16, true, false>(p, B, s);
-    return out_f32 ? launch_main<16, false, true>(p, B, s)
-                   : launch_main<16, false, false>(p, B, s);
-  }
-  if (local)
-    return out_f32 ? launch_main<8, true, true>(p, B, s)
-                   : launch_main<8, true, false>(p, B, s);
-  return out_f32 ? launch_main<8, false, true>(p, B, s)
-                 : launch_main<8, false, false>(p, B, s);
+  return out_f32 ? launch_main<false, true>(p, B, s)
+                 : launch_main<false, false>(p, B, s);
 }
 
 }  // namespace gqa

@@ -87,6 +87,7 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
 // few thousand, bf16 output) and speculative verification (n <= 16, fp32
 // output, keys split across workgroups).
 constexpr int kBlkTile = 64;               // keys per tile
+constexpr int kBlkQpw = 16;                // query tokens per workgroup
 constexpr int kMaxPrefill = GQA_MAX_CONTEXT;
 
 struct BlockPlan {
