@@ -76,7 +76,9 @@ BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify) {
   if (splits > 1 && splits > tiles / 2) splits = tiles / 2 > 1 ? tiles / 2 : 1;
   if (splits < 1) splits = 1;
   p.splits = (int)splits;
-  p.klin_bytes = kind == GQA_LOCAL
+  // local layers without key splits read pre-rotated keys from the
+  // workspace; split calls rotate each tile in LDS
+  p.klin_bytes = kind == GQA_LOCAL && p.splits == 1
                      ? align256((size_t)B * ((size_t)kW + n) * kTokenElems * 2)
                      : 0;
   p.part_bytes = p.splits > 1

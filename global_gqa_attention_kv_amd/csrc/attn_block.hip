@@ -60,6 +60,7 @@ constexpr int kPartRow = 132;               // floats: o[128], m, l, pad
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
 // Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
 // address lds + 16 l (lds wave-uniform).  Inline assembly, so the compiler
@@ -239,10 +240,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
   const uint16_t* kl_base =
       p.k_lin + (int64_t)b * p.klin_rows * kTokenElems + g * kD;
 
+  // Local layers read their keys rotated: from the pre-rotated copy in the
+  // workspace (KLIN, prefill: a key serves many workgroups), or raw from the
+  // ring and the block, rotated in LDS once a tile lands (ROTK, split
+  // verification: each key serves one workgroup).
+  constexpr bool ROTK = LOCAL && SPLIT;
+  constexpr bool KLIN = LOCAL && !SPLIT;
   auto k_src = [&](int j) -> const uint16_t* {
-    if (LOCAL) return kl_base + (j - klin0) * kTokenElems;
-    return j < pos0 ? kc_base + j * kTokenElems
-                    : kb_base + (j - pos0) * kTokenElems;
+    if (KLIN) return kl_base + (j - klin0) * kTokenElems;
+    if (j >= pos0) return kb_base + (j - pos0) * kTokenElems;
+    return kc_base + (LOCAL ? (j & (kW - 1)) : j) * kTokenElems;
   };
   auto v_src = [&](int j) -> const uint16_t* {
     if (j >= pos0) return vb_base + (j - pos0) * kTokenElems;
@@ -275,8 +282,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
     const int ring = LOCAL ? (kb & (kW - 1)) : kb;
     const uint16_t* kt =
         !full ? nullptr
-        : LOCAL ? kl_base + (kb - klin0) * kTokenElems
-        : in_cache ? kc_base + kb * kTokenElems
+        : KLIN ? kl_base + (kb - klin0) * kTokenElems
+        : in_cache ? (!LOCAL || ring + kBlkTile <= kW
+                          ? kc_base + ring * kTokenElems : nullptr)
         : in_blk ? kb_base + (kb - pos0) * kTokenElems : nullptr;
     const uint16_t* vt =
         !full ? nullptr
@@ -474,6 +482,43 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
 
+  // ROTK: thread i rotates item i of a landed K tile, item u = (key row
+  // u / 8, dims 8 (u % 8) .. + 7 against dims 64 + 8 (u % 8) ..), by the
+  // key's offset from p0 (the queries carry theirs); the sines and cosines
+  // are taken before the tile is waited for, so they overlap its load.
+  static_assert(!ROTK || WAVES * 64 == kBlkTile * 8, "one item per thread");
+  float rc[8], rs[8];
+  auto rope_angles = [&](int t) {
+    const int kb = k_lo + (t_begin + t) * kBlkTile;
+    const int j = min(kb + (tid >> 3), k_hi - 1);
+    const float delta = (float)(j - pos0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float r = delta * p.rope_rev[(tid & 7) * 8 + e];
+      r -= rintf(r);
+      sincos_rev(r, &rs[e], &rc[e]);
+    }
+  };
+  auto rope_tile = [&](auto SLOT) {
+    const int r = tid >> 3, cp = tid & 7;
+    lds_u32x4_t* lo = reinterpret_cast<lds_u32x4_t*>(
+        lds_base + SLOT * kSlotB + r * 256 + ((cp ^ (r & 15)) << 4));
+    lds_u32x4_t* hi = reinterpret_cast<lds_u32x4_t*>(
+        lds_base + SLOT * kSlotB + r * 256 + (((cp + 8) ^ (r & 15)) << 4));
+    u32x4_t a = *lo, c = *hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = bf16_lo(a[e]), x1 = bf16_hi(a[e]);
+      const float y0 = bf16_lo(c[e]), y1 = bf16_hi(c[e]);
+      const float c0 = rc[2 * e], s0 = rs[2 * e];
+      const float c1 = rc[2 * e + 1], s1 = rs[2 * e + 1];
+      a[e] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+      c[e] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+    }
+    *lo = a;
+    *hi = c;
+  };
+
   // tile t -> slot t % RING, loaded RING - 1 tiles ahead; the loop is
   // unrolled RING times so every slot offset is a constant
   static_for<0, RING - 1>([&](auto T) {
@@ -483,6 +528,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
     static_for<0, RING>([&](auto S) {
       const int t = t0 + S;
       if (t < ntiles) {
+        if constexpr (ROTK) rope_angles(t);
         // tile t has landed (this wave's rows) once only the later tiles'
         // loads are outstanding; the barrier publishes every wave's rows
         // and frees the slot consumed in the previous step
@@ -494,6 +540,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
         if (t + RING - 1 < ntiles)
           issue_tile(t + RING - 1,
                      std::integral_constant<int, (S + RING - 1) % RING>{});
+        if constexpr (ROTK) {
+          rope_tile(S);
+          __syncthreads();
+        }
         consume(t, S);
       }
     });
@@ -658,10 +708,12 @@ hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
                         bool local, bool out_f32, int B, hipStream_t s) {
   if (plan.qpw != kBlkQpw || p.splits > kMaxSplits) return hipErrorInvalidValue;
   if (local) {
-    hipLaunchKernelGGL(rope_keys_kernel, dim3((unsigned)p.klin_rows, B),
-                       dim3(64), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (p.splits == 1) {  // keys rotated once into the workspace
+      hipLaunchKernelGGL(rope_keys_kernel, dim3((unsigned)p.klin_rows, B),
+                         dim3(64), 0, s, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     return out_f32 ? launch_main<true, true>(p, B, s)
                    : launch_main<true, false>(p, B, s);
   }
