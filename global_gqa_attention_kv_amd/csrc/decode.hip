@@ -498,8 +498,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   constexpr int kPer = kMaxSplits / 32;
   float ms[kPer], ls[kPer];
   float4 os[kPer];
+  const int nper = (p.splits + 31) / 32;  // batches holding a split
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
+    ms[i] = -INFINITY;
+    ls[i] = 0.0f;
+    os[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (i >= nper) continue;
     const int s = sl + 32 * i;
     const float* ps = base + (size_t)min(s, p.splits - 1) * pf;
     ms[i] = s < p.splits ? ps[hl] : -INFINITY;
