@@ -21,7 +21,7 @@ __all__ = [
     "LOCAL", "GLOBAL", "OP_DECODE", "OP_VERIFY", "OP_PREFILL", "MAX_VERIFY",
     "attn_verify", "attn_prefill", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
     "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
-    "attn_decode", "attn_decode_append", "workspace_bytes", "workspace", "status_string", "abi_version",
+    "attn_decode", "attn_decode_append", "attn_decode_dev", "workspace_bytes", "workspace", "status_string", "abi_version",
     "library_path", "layer_kind",
 ]
 
@@ -87,6 +87,9 @@ def _load():
         lib.gqa_attn_decode_append.restype = i32
         lib.gqa_attn_decode_append.argtypes = [L, p, p, p, p, i32, p, p,
                                                ctypes.c_size_t, p]
+        lib.gqa_attn_decode_dev.restype = i32
+        lib.gqa_attn_decode_dev.argtypes = [L, p, p, p, p, i64, i32, p, p,
+                                            ctypes.c_size_t, p]
         _lib = lib
     return _lib
 
@@ -240,6 +243,39 @@ def attn_decode_append(layer: Layer, q, k_new, v_new, pos, out=None, ws=None,
     return _decode_common(_load().gqa_attn_decode_append,
                           "gqa_attn_decode_append", layer, q, pos, out, ws,
                           stream, extra=(kp, vp))
+
+
+def attn_decode_dev(layer: Layer, q, pos_dev, max_pos, out=None, ws=None,
+                    k_new=None, v_new=None, stream=None):
+    """Decode with device-resident positions (for graph replays that
+    advance them).  pos_dev: int64 GPU tensor [B], read when the kernels
+    run; max_pos: host bound on every entry (a position outside 0..max_pos
+    gives NaN rows and appends nothing).  k_new / v_new: both None (attend
+    only) or bf16 [B, 1, 2, 128] (append at pos_dev, then attend).
+    Returns out: fp32 [B, 32, 128]."""
+    B = int(q.shape[0])
+    qp = _dev(q, torch.bfloat16, (B, HQ, D), "q")
+    pp = _dev(pos_dev, torch.int64, (B,), "pos_dev")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    kp = vp = None
+    if k_new is not None:
+        kp = _dev(k_new, torch.bfloat16, (B, 1, HKV, D), "k_new")
+        vp = _dev(v_new, torch.bfloat16, (B, 1, HKV, D), "v_new")
+    if out is None:
+        out = torch.empty((B, HQ, D), dtype=torch.float32, device=q.device)
+    op = _dev(out, torch.float32, (B, HQ, D), "out")
+    if ws is None:
+        ws = workspace(OP_DECODE, layer.kind, B, 1, int(max_pos) + 1,
+                       device=q.device)
+    wp = _dev(ws, ws.dtype, None, "ws")
+    rc = _load().gqa_attn_decode_dev(layer.c_ref, qp, kp, vp, pp,
+                                     int(max_pos), B, op, wp,
+                                     ws.numel() * ws.element_size(),
+                                     _stream(stream))
+    if rc != 0:
+        raise GqaError(rc, "gqa_attn_decode_dev")
+    return out
 
 
 def _block_common(fn, name, op, out_dtype, layer, q, k_blk, v_blk, pos0, out,

@@ -160,9 +160,22 @@ int gqa_kv_append(const gqa_layer* layer, const void* k_new, const void* v_new,
 static int decode_impl(const gqa_layer* layer, const void* q,
                        const void* k_new, const void* v_new,
                        const int64_t* pos, int B, float* out, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, void* stream,
+                       const int64_t* pos_dev = nullptr,
+                       int64_t max_pos = 0) {
   int64_t max_keys = 0;
-  int rc = check_decode(layer, q, pos, B, out, &max_keys);
+  int rc;
+  if (pos_dev) {
+    // the kernels read the positions; the host checks the bound they are
+    // held to, exactly as it checks a position
+    if ((uintptr_t)pos_dev & 7u) return GQA_ERR_MISALIGNED;
+    int64_t bound[kMaxBatch];
+    if (B < 1 || B > GQA_MAX_BATCH) return GQA_ERR_INVALID_ARG;
+    for (int b = 0; b < B; ++b) bound[b] = max_pos;
+    rc = check_decode(layer, q, bound, B, out, &max_keys);
+  } else {
+    rc = check_decode(layer, q, pos, B, out, &max_keys);
+  }
   if (rc != GQA_OK) return rc;
   if (k_new || v_new) {
     if (!k_new || !v_new) return GQA_ERR_INVALID_ARG;
@@ -199,7 +212,9 @@ static int decode_impl(const gqa_layer* layer, const void* q,
       p.rope_rev[c] = (float)(pow(layer->rope_theta, -(double)c / (kD / 2)) /
                               (2.0 * 3.14159265358979323846));
   }
-  for (int b = 0; b < B; ++b) p.pos[b] = pos[b];
+  p.pos_dev = pos_dev;
+  p.max_pos = max_pos;
+  for (int b = 0; b < B; ++b) p.pos[b] = pos_dev ? max_pos : pos[b];
   hipError_t e = launch_decode(p, plan, local, B, (hipStream_t)stream);
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
@@ -218,6 +233,15 @@ int gqa_attn_decode_append(const gqa_layer* layer, const void* q,
   if (!k_new || !v_new) return GQA_ERR_INVALID_ARG;
   return decode_impl(layer, q, k_new, v_new, pos, B, out, ws, ws_bytes,
                      stream);
+}
+
+int gqa_attn_decode_dev(const gqa_layer* layer, const void* q,
+                        const void* k_new, const void* v_new,
+                        const int64_t* pos_dev, int64_t max_pos, int B,
+                        float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!pos_dev) return GQA_ERR_INVALID_ARG;
+  return decode_impl(layer, q, k_new, v_new, nullptr, B, out, ws, ws_bytes,
+                     stream, pos_dev, max_pos);
 }
 
 static int block_impl(const gqa_layer* layer, const void* q,

@@ -138,7 +138,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   const int g = bg % kHkv;
   const int b = bg / kHkv;
 
-  const int64_t pos = p.pos[b];
+  // positions come with the call, or from device memory (checked against
+  // the bound the host validated; a position outside it is not attended)
+  int64_t pos = p.pos[b];
+  bool pos_ok = true;
+  if (p.pos_dev) {
+    pos = p.pos_dev[b];
+    pos_ok = pos >= 0 && pos <= p.max_pos;
+    if (!pos_ok) pos = 0;
+  }
   // key index k is position j_first + k
   const int64_t j_first = LOCAL ? (pos > kW - 1 ? pos - (kW - 1) : 0) : 0;
   const int nkeys = (int)(pos - j_first + 1);
@@ -149,6 +157,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   const int new_key = nkeys - 1;
   const bool use_new = p.k_new != nullptr;
   float* const part = p.part + ((size_t)bg * p.splits + split) * PF;
+
+  if (!pos_ok) {  // NaN partials make the merged output NaN; no append
+    for (int i = tid; i < PF; i += NT) part[i] = __builtin_nanf("");
+    return;
+  }
 
   // The call appends the query's own token: one workgroup writes it to its
   // slot, which no other workgroup reads in this launch (they take that key

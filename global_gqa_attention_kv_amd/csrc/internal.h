@@ -76,6 +76,8 @@ struct DecodeParams {
   int32_t tiles_per_split;
   int32_t units;           // B * 2 * splits
   float rope_rev[kD / 2];  // local: theta^(-c/64) / (2 pi), revolutions per position
+  const int64_t* pos_dev;  // device positions [B] (read instead of pos), or null
+  int64_t max_pos;         // with pos_dev: positions above it are not attended
   int64_t pos[kMaxBatch];
 };
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,

@@ -129,6 +129,25 @@ int gqa_attn_decode_append(const gqa_layer* layer, const void* q,
                            const int64_t* pos, int B, float* out, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Decode with DEVICE-resident positions, for a step captured once in a HIP
+ * graph and replayed while the sequences advance (the caller updates
+ * pos_dev between replays, e.g. with an add kernel inside the graph).
+ * pos_dev: device int64 [B], read by the kernels when they run; max_pos:
+ * a host bound on every pos_dev[b], validated like a position (global:
+ * max_pos < capacity) -- it plans the key splits and sizes the workspace
+ * (gqa_workspace_bytes(GQA_OP_DECODE, kind, B, 1, max_pos + 1)).  k_new,
+ * v_new: both null (attend only, as gqa_attn_decode) or both given (append
+ * and attend, as gqa_attn_decode_append).  A device position outside
+ * [0, max_pos] is not attended: that sequence's output rows are NaN and
+ * nothing of it is appended.  Other arguments, layouts and the workspace
+ * rules as gqa_attn_decode.  Pages: shishifenxi.com section 01 (each new
+ * token reads the cached keys and values); runtimewire.com "Narrow cache"
+ * (a serving engine reuses one cache layout across steps). */
+int gqa_attn_decode_dev(const gqa_layer* layer, const void* q,
+                        const void* k_new, const void* v_new,
+                        const int64_t* pos_dev, int64_t max_pos, int B,
+                        float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Speculative verification of a drafted block of n (1..GQA_MAX_VERIFY)
  * tokens per sequence at positions pos0[b] .. pos0[b]+n-1, in one pass.
  * q: [B][n][32][128] bf16; k_blk, v_blk: [B][n][2][128] bf16, the block's

@@ -177,6 +177,24 @@ def test_decode_append_validation(lib):
     assert call(ws_bytes=8) == E_WS
 
 
+def test_decode_dev_validation(lib):
+    """Device positions: the host checks the bound max_pos like a position
+    (the positions themselves are read by the kernels)."""
+    L = _layer()   # global, capacity 4096
+
+    def call(pos_dev=FAKE, max_pos=10, kn=None, vn=None, B=1, ws_bytes=1 << 30):
+        return lib.gqa_attn_decode_dev(ctypes.byref(L), FAKE, kn, vn, pos_dev,
+                                       max_pos, B, FAKE, FAKE, ws_bytes, None)
+    assert call(pos_dev=None) == E_ARG
+    assert call(pos_dev=FAKE + 4) == E_ALN
+    assert call(B=0) == E_ARG
+    assert call(max_pos=4096) == E_POS
+    assert call(max_pos=-1) == E_POS
+    assert call(kn=FAKE) == E_ARG            # k_new and v_new go together
+    need = ga.workspace_bytes(ga.OP_DECODE, ga.GLOBAL, 1, 1, 4096)
+    assert call(max_pos=4095, ws_bytes=need - 1) == E_WS
+
+
 @pytest.mark.parametrize("fn", ["gqa_attn_verify", "gqa_attn_prefill"])
 def test_block_validation(lib, fn):
     f = getattr(lib, fn)
