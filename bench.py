@@ -111,6 +111,7 @@ def build_decode_step(ga, torch, B, pos, seed=1003):
 
     step.local_only = step_kind(ga.LOCAL)
     step.global_only = step_kind(ga.GLOBAL)
+    step.knews, step.vnews = knews, vnews
     return kinds, layers, qs, outs, ws, positions, step
 
 
@@ -125,6 +126,36 @@ def check_step_outputs(ga, torch, layers, qs, outs, positions, kinds):
         if not diff <= 1e-6:
             raise RuntimeError("decode step output of layer %d differs from "
                                "an eager call by %g" % (l, diff))
+
+
+def bench_decode_b1(ga, torch, steps, warmup):
+    """Single-sequence decode steps (append + attend per layer, HIP graph):
+    one local + one global layer at context 4096, and all 52 layers at
+    contexts 32768 and 131072."""
+    res = {}
+    for ctx in (4096, 32768, CTX):
+        kinds, layers, qs, outs, ws, positions, step = build_decode_step(
+            ga, torch, 1, ctx - 1)
+        if ctx == 4096:
+            pair = [kinds.index(ga.LOCAL), kinds.index(ga.GLOBAL)]
+
+            def fn():
+                for l in pair:
+                    ga.attn_decode_append(layers[l], qs[l], step.knews[l],
+                                          step.vnews[l], positions, outs[l], ws)
+            ms, _ = time_graph(torch, fn, steps, warmup)
+            nbytes = sum(kv_bytes_step([kinds[l]], positions) for l in pair)
+            name, what = "b1_ctx4096_1local_1global", "2 layers"
+        else:
+            ms, _ = time_graph(torch, step, steps, warmup)
+            nbytes = kv_bytes_step(kinds, positions)
+            name, what = "b1_ctx%d_52layers" % ctx, "52 layers"
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"us_per_step": round(ms * 1000, 2), "kv_GBps": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "layers": what}
+        del layers, qs, outs, ws, step
+        torch.cuda.empty_cache()
+    return res
 
 
 def time_graph(torch, fn, steps, warmup):
@@ -418,6 +449,8 @@ def main():
         print("# verify done", file=sys.stderr, flush=True)
         del layers, qs, outs, ws, step
         torch.cuda.empty_cache()
+        line["decode_b1"] = bench_decode_b1(ga, torch, args.steps, args.warmup)
+        print("# single-sequence decode done", file=sys.stderr, flush=True)
         line["prefill"] = bench_prefill(ga, torch)
         print("# prefill done", file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
