@@ -24,7 +24,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 DecodePlan plan_decode(int kind, int B, int64_t max_keys) {
   const int64_t tiles = (max_keys + kDecTile - 1) / kDecTile;
   DecodePlan p;
+  p.heads_per_wg = kGroup;
   if (kind == GQA_LOCAL) {
+    if (B <= kLocalSmallMaxBatch) p.heads_per_wg = kLocalSmallHeads;
     // the window is 32 tiles: one tile per workgroup up to batch 4 (256
     // workgroups), then longer splits so a launch stays near 256
     p.tiles_per_split = B >= 8 ? B / 4 : 1;
@@ -44,9 +46,10 @@ DecodePlan plan_decode(int kind, int B, int64_t max_keys) {
   return p;
 }
 
-// Workspace: the partial sums [B][2][splits][16 x 130] floats.
+// Workspace: the partial sums [B][2][head groups][splits][heads x 130]
+// floats (m[heads], l[heads], o[heads][128] per split).
 size_t decode_ws_bytes(int B, const DecodePlan& plan) {
-  return align256((size_t)B * kHkv * plan.splits * kPartFloats *
+  return align256((size_t)B * kHkv * plan.splits * kGroup * (kD + 2) *
                   sizeof(float));
 }
 

@@ -112,14 +112,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // LOCAL: the keys are the window max(0, pos - 2047) .. pos read through the
 // ring, and each landed K tile is rotated in LDS by its keys' offsets to the
 // query before the products.
-template <int WAVES, int RING, bool LOCAL>
+template <int WAVES, int HPW, int RING, bool LOCAL>
 __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     const DecodeParams p) {
   constexpr int NT = 64 * WAVES;
-  constexpr int HW = kGroup / WAVES;  // query heads per wave
+  constexpr int HW = HPW / WAVES;     // query heads per wave
+  constexpr int HG = kGroup / HPW;    // workgroups sharing a tile (head groups)
   constexpr int LPH = 16 / HW;        // lanes per head in the q broadcast rows
   constexpr int PPL = 4 * HW;         // q pairs per lane
-  constexpr int PF = kGroup * (kD + 2);
+  constexpr int PF = HPW * (kD + 2);
   constexpr int RPW = kDecTile / WAVES;   // tile rows each wave loads
   constexpr int LPT = RPW / 4;            // loads per K (or V) tile per wave
   constexpr int PSW = (kDecTile / 2) * HW * 4;  // P bytes per wave
@@ -131,8 +132,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint8_t* Ps = smem + RING * kSlotBytes + w * PSW;
 
-  const int unit = blockIdx.x;
-  if (unit >= p.units) return;
+  // workgroup -> (unit, head group).  Consecutive workgroup ids go to
+  // different XCDs round-robin, so the HG workgroups of one unit are placed
+  // 8 ids apart: same XCD, same L2, dispatched together.
+  int unit = blockIdx.x, hg = 0;
+  if constexpr (HG > 1) {
+    const int r = blockIdx.x % (8 * HG);
+    unit = (blockIdx.x / (8 * HG)) * 8 + (r & 7);
+    hg = r >> 3;
+  }
+  if (unit >= p.units) return;  // padding of the XCD-aware grid
   const int split = unit % p.splits;
   const int bg = unit / p.splits;  // b * 2 + g
   const int g = bg % kHkv;
@@ -156,7 +165,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   const bool has_keys = k_begin < nkeys;
   const int new_key = nkeys - 1;
   const bool use_new = p.k_new != nullptr;
-  float* const part = p.part + ((size_t)bg * p.splits + split) * PF;
+  float* const part =
+      p.part + (((size_t)bg * HG + hg) * p.splits + split) * PF;
 
   if (!pos_ok) {  // NaN partials make the merged output NaN; no append
     for (int i = tid; i < PF; i += NT) part[i] = __builtin_nanf("");
@@ -166,7 +176,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   // The call appends the query's own token: one workgroup writes it to its
   // slot, which no other workgroup reads in this launch (they take that key
   // from k_new / v_new).
-  if (use_new && g == 0 && has_keys && new_key / span == split && tid < 64) {
+  if (use_new && g == 0 && hg == 0 && has_keys && new_key / span == split &&
+      tid < 64) {
     const bool is_v = tid >= 32;
     const int chunk = tid & 31;
     const uint16_t* src = (is_v ? p.v_new : p.k_new) +
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   }
 
   if (!has_keys) {
-    for (int i = tid; i < PF; i += NT) part[i] = i < kGroup ? -INFINITY : 0.0f;
+    for (int i = tid; i < PF; i += NT) part[i] = i < HPW ? -INFINITY : 0.0f;
     return;
   }
 
@@ -186,7 +197,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   const uint16_t* Vb = p.v + (int64_t)b * p.seq_stride + g * kD;
   const uint16_t* Kn = p.k_new + (int64_t)b * kTokenElems + g * kD;
   const uint16_t* Vn = p.v_new + (int64_t)b * kTokenElems + g * kD;
-  const int head0 = g * kGroup + w * HW;
+  const int head0 = g * kGroup + hg * HPW + w * HW;
 
   // The wave's HW query rows (64 bf16 pairs each) held as wave-uniform words
   // for the DPP broadcast: within every 16-lane row, lane n keeps pairs
@@ -431,6 +442,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     }
   };
 
+  if constexpr (RING == 1) {
+    // one tile per workgroup (the planner guarantees it): load, wait, use
+    if (ntiles > 0) {
+      issue_tile(0, std::integral_constant<int, 0>{});
+      if constexpr (LOCAL) rope_angles(0);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if constexpr (LOCAL) {
+        rope_tile(std::integral_constant<int, 0>{});
+        __syncthreads();
+      }
+      consume(0, std::integral_constant<int, 0>{});
+    }
+  } else {
   static_for<0, RING - 1>([&](auto T) {
     if (T < ntiles) issue_tile(T, T);
   });
@@ -458,6 +483,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
       }
     });
   }
+  }  // RING > 1
 
   // ---- reduce over the four key groups and the 64 key lanes, write
 #pragma unroll
@@ -472,7 +498,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   if (kg == 0) {
 #pragma unroll
     for (int hl = 0; hl < HW; ++hl) {
-      float* dst = part + 2 * kGroup + (w * HW + hl) * kD + jl;
+      float* dst = part + 2 * HPW + (w * HW + hl) * kD + jl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dst[16 * e] = o[hl][e];
     }
@@ -481,7 +507,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
 #pragma unroll
     for (int hl = 0; hl < HW; ++hl) {
       part[w * HW + hl] = m[hl];
-      part[kGroup + w * HW + hl] = lsum[hl];
+      part[HPW + w * HW + hl] = lsum[hl];
     }
   }
 }
@@ -494,13 +520,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
 // first (wave maximum, then across the four waves), so the weighted sums
 // need no rescaling and the split lanes combine by plain addition.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
-    const DecodeParams p) {
+    const DecodeParams p, int hpw) {
   const int dq = blockIdx.x & 3;
   const int h = (blockIdx.x >> 2) % kHq;
   const int b = (blockIdx.x >> 2) / kHq;
-  const int g = h / kGroup, hl = h % kGroup;
-  constexpr int pf = kGroup * (kD + 2);
-  const float* base = p.part + (size_t)(b * kHkv + g) * p.splits * pf;
+  const int g = h / kGroup, hh = h % kGroup;
+  const int hg = hh / hpw, hl = hh % hpw;  // head group, head within it
+  const int pf = hpw * (kD + 2);
+  const float* base =
+      p.part + ((size_t)(b * kHkv + g) * (kGroup / hpw) + hg) * p.splits * pf;
   const int tid = threadIdx.x;
   const int c4 = tid & 7, sl = tid >> 3, w = tid >> 6;
   const int d = dq * 32 + c4 * 4;
@@ -521,8 +549,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int s = sl + 32 * i;
     const float* ps = base + (size_t)min(s, p.splits - 1) * pf;
     ms[i] = s < p.splits ? ps[hl] : -INFINITY;
-    ls[i] = ps[kGroup + hl];
-    os[i] = *reinterpret_cast<const float4*>(ps + 2 * kGroup + hl * kD + d);
+    ls[i] = ps[hpw + hl];
+    os[i] = *reinterpret_cast<const float4*>(ps + 2 * hpw + hl * kD + d);
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -579,17 +607,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
                          bool local, int B, hipStream_t s) {
-  (void)plan;
-  if (local)
-    hipLaunchKernelGGL((decode_split_kernel<kLocalWaves, 2, true>),
+  if (local && plan.heads_per_wg == kLocalSmallHeads) {
+    // small batches: 4 workgroups (head groups) share each tile
+    constexpr int HG = kGroup / kLocalSmallHeads;
+    const int grid = (p.units + 7) / 8 * 8 * HG;
+    if (p.tiles_per_split != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(
+        (decode_split_kernel<kLocalSmallWaves, kLocalSmallHeads, 1, true>),
+        dim3(grid), dim3(64 * kLocalSmallWaves), 0, s, p);
+  } else if (local) {
+    hipLaunchKernelGGL((decode_split_kernel<kLocalWaves, kGroup, 2, true>),
                        dim3(p.units), dim3(64 * kLocalWaves), 0, s, p);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<kGlobalWaves, kGlobalRing, false>),
-                       dim3(p.units), dim3(64 * kGlobalWaves), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(
+        (decode_split_kernel<kGlobalWaves, kGroup, kGlobalRing, false>),
+        dim3(p.units), dim3(64 * kGlobalWaves), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(B * kHq * 4), dim3(256), 0, s,
-                     p);
+                     p, plan.heads_per_wg);
   return hipGetLastError();
 }
 

@@ -47,6 +47,12 @@ constexpr int kGlobalWGsPerCU = kGlobalRing <= 2 ? 2 : 1;
 // Local-layer decode (latency-bound, one tile per workgroup): 8 waves of 2
 // heads put more waves behind each tile than 4 waves of 4 heads.
 constexpr int kLocalWaves = 8;
+// Local layers at small batch: the 16 heads of a KV head split over 4
+// workgroups of 2 waves (2 heads each), which read the same tile (L2 hits
+// after the first) and each do a quarter of the products.
+constexpr int kLocalSmallHeads = 4;
+constexpr int kLocalSmallWaves = 2;
+constexpr int kLocalSmallMaxBatch = 2;
 // Most key splits of one decode call (the merge kernel loads them all at once).
 constexpr int kMaxSplits = 256;
 
@@ -55,10 +61,10 @@ constexpr int kMaxSplits = 256;
 struct DecodePlan {
   int splits;           // S: key splits per (sequence, KV head)
   int tiles_per_split;  // tiles of kDecTile keys per split
+  int heads_per_wg;     // 16, or kLocalSmallHeads (head groups share a tile)
 };
 DecodePlan plan_decode(int kind, int B, int64_t max_keys);
 size_t decode_ws_bytes(int B, const DecodePlan& plan);
-constexpr int kPartFloats = kGroup * (kD + 2);  // m[16], l[16], o[16][128]
 
 struct DecodeParams {
   const uint16_t* k;       // cache base (sequence 0, slot 0, head 0)
