@@ -10,10 +10,7 @@
 namespace gqa {
 
 namespace {
-// Wide decode launches aim for about this many workgroups so every compute
-// unit holds a few resident workgroups; each workgroup then streams several
-// tiles.
-// Global-layer decode: as many wide-kernel workgroups as fit the 256 CUs at
+// Global-layer decode: as many split-kernel workgroups as fit the 256 CUs at
 // once, so the launch runs as one full round (a partial second round would
 // leave part of the device idle at the end).
 constexpr int kDecodeTargetWGs = 256 * kGlobalWGsPerCU;

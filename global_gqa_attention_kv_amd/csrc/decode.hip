@@ -108,7 +108,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 }
 
-// WAVES waves share the 16 query heads (16 / WAVES each); RING tile slots.
+// A workgroup of WAVES waves serves HPW of the 16 query heads (HPW / WAVES
+// per wave; 16 / HPW workgroups share each tile); RING tile slots.
 // LOCAL: the keys are the window max(0, pos - 2047) .. pos read through the
 // ring, and each landed K tile is rotated in LDS by its keys' offsets to the
 // query before the products.
