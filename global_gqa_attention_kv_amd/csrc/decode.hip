@@ -15,11 +15,12 @@
 //    workgroups per CU, long splits; local layers (a 2048-key window, so
 //    latency rather than bandwidth): 8 waves of 2 heads, one 64-key tile per
 //    workgroup up to batch 4.
-//  * Tiles of 64 keys go straight from HBM into a two-slot LDS ring with
-//    direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land at
-//    the wave's LDS base + 16 l, never passing through VGPRs), marked
-//    non-temporal since the cache is streamed once per step; tile t + 1 is in
-//    flight while tile t is consumed.
+//  * Tiles of 64 keys go straight from HBM into LDS rings with direct-to-LDS
+//    loads (global_load_lds_dwordx4: lane l's 16 bytes land at the wave's LDS
+//    base + 16 l, never passing through VGPRs), marked non-temporal since the
+//    cache is streamed once per step.  K and V tiles have rings of their own;
+//    on global layers K tiles are loaded two tiles ahead and V tiles one
+//    (three K slots, two V slots: 80 KB, two workgroups per CU).
 //  * Q.K: lane = key; the query words are wave-uniform, held 16 to a VGPR
 //    and broadcast with DPP row_newbcast into v_dot2c_f32_bf16 (bf16
 //    products exact, fp32 accumulation).  K rows sit in LDS with 16-byte
@@ -35,8 +36,10 @@
 //    exceeds it by more than 2^8, which keeps every exponent <= 2^8 while
 //    skipping nearly all cross-lane reductions.  The denominator sums exactly
 //    the bf16 weights the P.V product uses.
-//  * P.V: P goes to wave-private LDS as bf16 key pairs; V rows stay in key
-//    order (chunk c at slot c ^ 2(r & 7)) and are read with
+//  * P.V: each 16-lane row of a wave takes the 16 keys whose scores it holds;
+//    the bf16 weights of a key pair are packed into one lane and broadcast to
+//    the row with DPP row_newbcast (P never goes through LDS).  V rows stay in
+//    key order (chunk c at slot c ^ 2(r & 7)) and are read with
 //    ds_read_b64_tr_b16, which gives each lane four consecutive keys of one
 //    dimension: two key-interleaved bf16 pairs, the operand v_dot2_f32_bf16
 //    wants, with no VALU re-packing.
@@ -58,12 +61,11 @@ __device__ __forceinline__ int64_t slot_of(int64_t position, bool local) {
   return local ? (position & (kW - 1)) : position;
 }
 
-// The tile loop is unrolled RING times so every LDS address is a per-lane
-// register plus a constant.  P.V lanes: lane 16 g + j owns dimensions j,
-// j + 16, ..., j + 112 of its wave's heads and keys 16 q + 4 g .. + 3 of each
-// 16-key quarter q; the four groups g are summed at the end.
+// The tile loop is unrolled over the period of the slot pattern so every LDS
+// address is a per-lane register plus a constant.  P.V lanes: lane 16 g + j
+// owns dimensions j, j + 16, ..., j + 112 of its wave's heads and keys
+// 16 g .. 16 g + 15; the four rows g are summed at the end.
 constexpr int kTileBytes = kDecTile * 256;    // one 64-key tile of K or V
-constexpr int kSlotBytes = 2 * kTileBytes;    // K tile, then V tile
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
@@ -109,11 +111,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // A workgroup of WAVES waves serves HPW of the 16 query heads (HPW / WAVES
-// per wave; 16 / HPW workgroups share each tile); RING tile slots.
-// LOCAL: the keys are the window max(0, pos - 2047) .. pos read through the
-// ring, and each landed K tile is rotated in LDS by its keys' offsets to the
-// query before the products.
-template <int WAVES, int HPW, int RING, bool LOCAL>
+// per wave; 16 / HPW workgroups share each tile); KR slots for K tiles and
+// VR for V tiles (K tiles are needed first in a step, so they may be loaded
+// one tile further ahead).  LOCAL: the keys are the window
+// max(0, pos - 2047) .. pos read through the ring, and each landed K tile is
+// rotated in LDS by its keys' offsets to the query before the products.
+template <int WAVES, int HPW, int KR, int VR, bool LOCAL>
 __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     const DecodeParams p) {
   constexpr int NT = 64 * WAVES;
@@ -124,14 +127,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   constexpr int PF = HPW * (kD + 2);
   constexpr int RPW = kDecTile / WAVES;   // tile rows each wave loads
   constexpr int LPT = RPW / 4;            // loads per K (or V) tile per wave
-  constexpr int PSW = (kDecTile / 2) * HW * 4;  // P bytes per wave
-  static_assert(HW == 2 || HW == 4, "P reads assume 2 or 4 heads per wave");
-  __shared__ __attribute__((aligned(16)))
-  uint8_t smem[RING * kSlotBytes + WAVES * PSW];
+  static_assert(HW == 2 || HW == 4, "two or four heads per wave");
+  static_assert(KR == VR || KR == VR + 1, "K at most one tile further ahead");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(KR + VR) * kTileBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* Ps = smem + RING * kSlotBytes + w * PSW;
 
   // workgroup -> (unit, head group).  Consecutive workgroup ids go to
   // different XCDs round-robin, so the HG workgroups of one unit are placed
@@ -226,9 +227,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
 #pragma unroll
   for (int v = 0; v < PPL; ++v) asm volatile("" : "+v"(qv[v]));
 
-  // Tile t -> slot t % RING.  Wave w fills rows RPW w .. RPW (w+1) - 1 of
-  // the K and V tiles, four rows (1 KB) per load: lane l takes row
-  // RPW w + 4i + l/16 and chunk slot l % 16.
+  // Tile t -> K slot t % KR, V slot t % VR.  Wave w fills rows
+  // RPW w .. RPW (w+1) - 1 of the K and V tiles, four rows (1 KB) per load:
+  // lane l takes row RPW w + 4i + l/16 and chunk slot l % 16.
   const int rsub = lane >> 4, cs = lane & 15;
   uint32_t kdma[LPT], vdma[LPT];  // byte offsets from the tile's first key
 #pragma unroll
@@ -237,38 +238,43 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     kdma[i] = row * (kTokenElems * 2) + ((cs ^ (row & 15)) << 4);
     vdma[i] = row * (kTokenElems * 2) + ((cs ^ (2 * (row & 7))) << 4);
   }
+  // K slot k at lds_base + k * kTileBytes, V slot v at vbase + v * kTileBytes
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
-  auto issue_tile = [&](int t, auto SLOT) {
+  const uint32_t vbase = lds_base + KR * kTileBytes;
+  // Wave w's rows of tile t of K (IS_V false) or V into LDS at lds.  A full
+  // tile of cached keys in consecutive slots loads from one wave-uniform
+  // base; the split's last tile repeats its last key past the end (masked)
+  // and takes the query's own key from k_new / v_new.
+  auto issue = [&](int t, auto IS_V, uint32_t lds) {
+    const uint16_t* base = IS_V ? Vb : Kb;
+    const uint16_t* fresh_row = IS_V ? Vn : Kn;
     const int kb = k_begin + t * kDecTile;
-    const uint32_t kl = __builtin_amdgcn_readfirstlane(
-        lds_base + SLOT * kSlotBytes + w * RPW * 256);
     const int64_t slot0 = slot_of(j_first + kb, LOCAL);
+    lds = __builtin_amdgcn_readfirstlane(lds + w * RPW * 256);
     if (kb + kDecTile <= k_end && (!use_new || new_key >= kb + kDecTile) &&
         (!LOCAL || slot0 + kDecTile <= kW)) {
-      // a full tile of cached keys in consecutive slots
-      const uint16_t* kt = Kb + slot0 * kTokenElems;
-      const uint16_t* vt = Vb + slot0 * kTokenElems;
+      const uint16_t* tb = base + slot0 * kTokenElems;
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        dma16(kt, kdma[i], kl + i * 1024);
-        dma16(vt, vdma[i], kl + kTileBytes + i * 1024);
-      }
+      for (int i = 0; i < LPT; ++i)
+        dma16(tb, IS_V ? vdma[i] : kdma[i], lds + i * 1024);
     } else {
-      // the split's last tile: keys past its end repeat the last key (they
-      // are masked), and the query's own key comes from k_new / v_new
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int row = RPW * w + 4 * i + rsub;
         const int key = min(kb + row, k_end - 1);
         const bool fresh = use_new && key == new_key;
         const int64_t slot = slot_of(j_first + key, LOCAL);
-        const uint16_t* krow = fresh ? Kn : Kb + slot * kTokenElems;
-        const uint16_t* vrow = fresh ? Vn : Vb + slot * kTokenElems;
-        dma16(krow + ((cs ^ (row & 15)) << 3), kl + i * 1024);
-        dma16(vrow + ((cs ^ (2 * (row & 7))) << 3),
-              kl + kTileBytes + i * 1024);
+        const uint16_t* src = fresh ? fresh_row : base + slot * kTokenElems;
+        const int c = IS_V ? cs ^ (2 * (row & 7)) : cs ^ (row & 15);
+        dma16(src + (c << 3), lds + i * 1024);
       }
     }
+  };
+  auto issue_k = [&](int t, auto KS) {
+    issue(t, std::false_type{}, lds_base + KS * kTileBytes);
+  };
+  auto issue_v = [&](int t, auto VS) {
+    issue(t, std::true_type{}, vbase + VS * kTileBytes);
   };
 
   float m[HW], lsum[HW], o[HW][8];
@@ -276,26 +282,27 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   for (int hl = 0; hl < HW; ++hl) {
     m[hl] = -INFINITY;
     lsum[hl] = 0.0f;
+    // each accumulator gets a register of its own (a shared zero would be
+    // copied in right before the first DPP product that reads it)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[hl][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) asm volatile("v_mov_b32 %0, 0" : "=v"(o[hl][e]));
   }
 
-  // LDS read offsets: the K row of key = lane, and the P.V transposes (the
-  // 16-lane group kg reads keys 16q + 4kg + (j >> 2), dims 16e + 4(j & 3)).
+  // LDS read offsets: the K row of key = lane, and the P.V transposes: row
+  // kg of the wave (lanes 16 kg ..) reads keys 16 kg + 4 q + (j >> 2), dims
+  // 16 e + 4 (j & 3) for key quad q of its row; for odd q the swizzle puts
+  // dims 16 e at the offset of dims 16 (e ^ 4) of q = 0.
   const int kg = lane >> 4, jl = lane & 15, ja = jl & 3, je = jl >> 2;
   uint32_t krd[16], vrd[8];
 #pragma unroll
   for (int c = 0; c < 16; ++c) krd[c] = lds_base + lane * 256 + ((c ^ jl) << 4);
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    vrd[e] = lds_base + kTileBytes + (4 * kg + je) * 256 +
-             32 * (e ^ ((4 * kg + je) & 7)) +
-             8 * ja;
-  // P words of key pairs 8q + 2kg and 8q + 2kg + 1
-  const uint32_t prd = (uint32_t)(uintptr_t)Ps + 2 * kg * HW * 4;
+    vrd[e] = vbase + (16 * kg + je) * 256 + 32 * (e ^ je) + 8 * ja;
 
-  auto consume = [&](int t, auto SLOT) {
-    constexpr uint32_t so = SLOT * kSlotBytes;
+  auto consume = [&](int t, auto KS, auto VS) {
+    constexpr uint32_t so = KS * kTileBytes;
+    constexpr uint32_t vso = VS * kTileBytes;
     // ---- scores: lane = key of this tile; the query word of (head hl,
     // pair pr) is broadcast from lane hl * LPH + pr / PPL.  The lane's K row
     // is read from LDS in 4 batches of 64 B, one batch ahead of the
@@ -333,6 +340,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
       });
     });
     static_assert(HW * NACC == 4, "four score accumulators per wave");
+    // V^T operands of key quad QQ of the row (see P.V below); the first
+    // quad's are read before the softmax, each next quad's one quad ahead
+    uint2 vw[2][8];
+    auto read_quad = [&](auto QQ, uint2(&dst)[8]) {
+      static_for<0, 8>([&](auto E) {
+        constexpr int e = (QQ & 1) ? (E ^ 4) : E;
+        const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_v4i16_t*>(vrd[e] + vso + QQ * 1024));
+        dst[E] = __builtin_bit_cast(uint2, r);
+      });
+    };
+    read_quad(std::integral_constant<int, 0>{}, vw[0]);
     dpp_settle(acc[0][0], acc[(1 / NACC) % HW][1 % NACC],
                acc[(2 / NACC) % HW][2 % NACC], acc[(3 / NACC) % HW][3 % NACC]);
     const bool valid = k_begin + t * kDecTile + lane < k_end;
@@ -357,46 +376,48 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
         for (int e = 0; e < 8; ++e) o[hl][e] *= alpha;
       }
     }
-    uint16_t* P16 = reinterpret_cast<uint16_t*>(Ps);
+    // ---- P.V.  Lane 16 r + j takes the 16 keys of its own row r and
+    // dimensions j, j + 16, ..., j + 112.  The bf16 weights of key pair i of
+    // the row (keys 2i, 2i + 1) are packed into lane 2i and broadcast to the
+    // row with DPP row_newbcast, so P never goes through LDS.
+    uint32_t pk[HW];
 #pragma unroll
     for (int hl = 0; hl < HW; ++hl) {
-      const uint16_t pb = to_bf16(fast_exp2(s2[hl] - m[hl]));
-      lsum[hl] += __builtin_bit_cast(float, (uint32_t)pb << 16);
-      P16[(lane >> 1) * (2 * HW) + hl * 2 + (lane & 1)] = pb;
+      const uint32_t pb = to_bf16(fast_exp2(s2[hl] - m[hl]));
+      lsum[hl] += __builtin_bit_cast(float, pb << 16);
+      // lanes 2i take lane 2i + 1's weight (quad_perm [1, 1, 3, 3])
+      const uint32_t nb = __builtin_amdgcn_mov_dpp((int)pb, 0xF5, 0xF, 0xF, false);
+      pk[hl] = pb | (nb << 16);
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P visible to the wave
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- P.V over the four 16-key quarters of the tile
-    static_for<0, 4>([&](auto Q) {
-      uint32_t pa[HW], pc[HW];  // pairs 8Q + 2kg and 8Q + 2kg + 1
-      if constexpr (HW == 4) {
-        const u32x4_t x = *reinterpret_cast<const lds_u32x4_t*>(prd + Q * 128);
-        const u32x4_t y =
-            *reinterpret_cast<const lds_u32x4_t*>(prd + Q * 128 + 16);
-        static_for<0, 4>([&](auto H) {
-          constexpr int h = H;
-          pa[h] = x[h];
-          pc[h] = y[h];
-        });
-      } else {
-        const u32x4_t x = *reinterpret_cast<const lds_u32x4_t*>(prd + Q * 64);
-        pa[0] = x[0];
-        pa[1] = x[1];
-        pc[0] = x[2];
-        pc[1] = x[3];
-      }
+    // two wait states between the last VALU write of a weight pair and the
+    // DPP products that read it
+    if constexpr (HW == 4)
+      asm volatile("s_nop 1" : "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]), "+v"(pk[3]));
+    else
+      asm volatile("s_nop 1" : "+v"(pk[0]), "+v"(pk[1]));
+    static_for<0, 4>([&](auto QQ) {  // keys 4 QQ .. 4 QQ + 3 of the row
+      if constexpr (QQ + 1 < 4)
+        read_quad(std::integral_constant<int, QQ + 1>{}, vw[(QQ + 1) & 1]);
+      constexpr int cb = QQ & 1;
+      // keys (4 QQ, 4 QQ + 1) for every accumulator, then (4 QQ + 2, + 3):
+      // a product's accumulator was last written HW * 8 products earlier
       static_for<0, 8>([&](auto E) {
-        const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<lds_v4i16_t*>(vrd[E] + so + Q * 16 * 256));
-        const uint2 vw = __builtin_bit_cast(uint2, r);
-#pragma unroll
-        for (int hl = 0; hl < HW; ++hl) {
-          o[hl][E] = dot2_bf16(pa[hl], vw.x, o[hl][E]);
-          o[hl][E] = dot2_bf16(pc[hl], vw.y, o[hl][E]);
-        }
+        static_for<0, HW>([&](auto HL) {
+          o[HL][E] =
+              dot2_bf16_bcast<4 * QQ, false>(pk[HL], vw[cb][E].x, o[HL][E]);
+        });
+      });
+      static_for<0, 8>([&](auto E) {
+        static_for<0, HW>([&](auto HL) {
+          o[HL][E] =
+              dot2_bf16_bcast<4 * QQ + 2, false>(pk[HL], vw[cb][E].y, o[HL][E]);
+        });
       });
     });
+    // the last four products' results settle before any plain read
+    constexpr int L0 = HW * 8 - 4;
+    dpp_settle(o[L0 % HW][L0 / HW], o[(L0 + 1) % HW][(L0 + 1) / HW],
+               o[(L0 + 2) % HW][(L0 + 2) / HW], o[(L0 + 3) % HW][(L0 + 3) / HW]);
   };
 
   // LOCAL: thread i rotates items i, i + NT, ... of the K tile, item u =
@@ -424,9 +445,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     for (int i = 0; i < RIT; ++i) {
       const int u = tid + i * NT, row = u >> 3, cp = u & 7;
       lds_u32x4_t* lo = reinterpret_cast<lds_u32x4_t*>(
-          lds_base + SLOT * kSlotBytes + row * 256 + ((cp ^ (row & 15)) << 4));
+          lds_base + SLOT * kTileBytes + row * 256 + ((cp ^ (row & 15)) << 4));
       lds_u32x4_t* hi = reinterpret_cast<lds_u32x4_t*>(
-          lds_base + SLOT * kSlotBytes + row * 256 +
+          lds_base + SLOT * kTileBytes + row * 256 +
           (((cp + 8) ^ (row & 15)) << 4));
       u32x4_t a = *lo, c = *hi;
 #pragma unroll
@@ -443,48 +464,63 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     }
   };
 
-  if constexpr (RING == 1) {
+  constexpr auto C0 = std::integral_constant<int, 0>{};
+  if constexpr (KR == 1) {
     // one tile per workgroup (the planner guarantees it): load, wait, use
     if (ntiles > 0) {
-      issue_tile(0, std::integral_constant<int, 0>{});
+      issue_k(0, C0);
+      issue_v(0, C0);
       if constexpr (LOCAL) rope_angles(0);
       wait_vmcnt<0>();
       __syncthreads();
       if constexpr (LOCAL) {
-        rope_tile(std::integral_constant<int, 0>{});
+        rope_tile(C0);
         __syncthreads();
       }
-      consume(0, std::integral_constant<int, 0>{});
+      consume(0, C0, C0);
     }
   } else {
-  static_for<0, RING - 1>([&](auto T) {
-    if (T < ntiles) issue_tile(T, T);
-  });
-  for (int t0 = 0; t0 < ntiles; t0 += RING) {
-    static_for<0, RING>([&](auto S) {
-      const int t = t0 + S;
-      if (t < ntiles) {
-        if constexpr (LOCAL) rope_angles(t);
-        // tile t has landed (this wave's rows) once only the later tiles'
-        // loads are outstanding; the barrier publishes every wave's rows
-        // and frees the slot consumed in the previous step
-        const int later = min(RING - 2, ntiles - 1 - t);
-        static_for<0, RING - 1>([&](auto L) {
-          if (later == L) wait_vmcnt<L * 2 * LPT>();
-        });
-        __syncthreads();
-        if (t + RING - 1 < ntiles)
-          issue_tile(t + RING - 1,
-                     std::integral_constant<int, (S + RING - 1) % RING>{});
-        if constexpr (LOCAL) {
-          rope_tile(S);
-          __syncthreads();
-        }
-        consume(t, S);
+    // Step s (after its barrier) loads V of tile s + VR - 1, then K of tile
+    // s + KR - 1, into the slots tile s - 1 used; the prologue issues what
+    // steps -(KR - 1) .. -1 would have.
+    constexpr int DK = KR - 1, DV = VR - 1;
+    constexpr int PER = KR == VR ? KR : KR * VR;  // slot pattern period
+    static_for<0, DK>([&](auto I) {
+      constexpr int s0 = I - DK;
+      if constexpr (s0 + DV >= 0) {
+        if (s0 + DV < ntiles)
+          issue_v(s0 + DV, std::integral_constant<int, (s0 + DV) % VR>{});
       }
+      if (s0 + DK < ntiles)
+        issue_k(s0 + DK, std::integral_constant<int, (s0 + DK) % KR>{});
     });
+    for (int t0 = 0; t0 < ntiles; t0 += PER) {
+      static_for<0, PER>([&](auto S) {
+        const int t = t0 + S;
+        if (t < ntiles) {
+          if constexpr (LOCAL) rope_angles(t);
+          // tile t has landed (this wave's rows) once at most the K tile
+          // issued after V of tile t is outstanding; the barrier publishes
+          // every wave's rows and frees the slots of tile t - 1
+          if (DK > DV && t + 1 < ntiles)
+            wait_vmcnt<LPT>();
+          else
+            wait_vmcnt<0>();
+          __syncthreads();
+          if (t + DV < ntiles)
+            issue_v(t + DV, std::integral_constant<int, (S + DV) % VR>{});
+          if (t + DK < ntiles)
+            issue_k(t + DK, std::integral_constant<int, (S + DK) % KR>{});
+          if constexpr (LOCAL) {
+            rope_tile(std::integral_constant<int, S % KR>{});
+            __syncthreads();
+          }
+          consume(t, std::integral_constant<int, S % KR>{},
+                  std::integral_constant<int, S % VR>{});
+        }
+      });
+    }
   }
-  }  // RING > 1
 
   // ---- reduce over the four key groups and the 64 key lanes, write
 #pragma unroll
@@ -614,14 +650,15 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
     const int grid = (p.units + 7) / 8 * 8 * HG;
     if (p.tiles_per_split != 1) return hipErrorInvalidValue;
     hipLaunchKernelGGL(
-        (decode_split_kernel<kLocalSmallWaves, kLocalSmallHeads, 1, true>),
+        (decode_split_kernel<kLocalSmallWaves, kLocalSmallHeads, 1, 1, true>),
         dim3(grid), dim3(64 * kLocalSmallWaves), 0, s, p);
   } else if (local) {
-    hipLaunchKernelGGL((decode_split_kernel<kLocalWaves, kGroup, 2, true>),
+    hipLaunchKernelGGL((decode_split_kernel<kLocalWaves, kGroup, 2, 2, true>),
                        dim3(p.units), dim3(64 * kLocalWaves), 0, s, p);
   } else {
     hipLaunchKernelGGL(
-        (decode_split_kernel<kGlobalWaves, kGroup, kGlobalRing, false>),
+        (decode_split_kernel<kGlobalWaves, kGroup, kGlobalKRing,
+                             kGlobalVRing, false>),
         dim3(p.units), dim3(64 * kGlobalWaves), 0, s, p);
   }
   hipError_t e = hipGetLastError();

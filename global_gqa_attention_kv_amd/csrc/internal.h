@@ -37,13 +37,15 @@ hipError_t launch_kv_append(const AppendParams& p, int B, int count,
 // ---------------------------------------------------------------- decode
 constexpr int kDecTile = 64;               // keys per tile
 // Global-layer decode: waves per workgroup (16 / waves query heads each),
-// tile slots in its LDS ring (32 KB each), and how many such workgroups fit
-// one CU.  Four waves with a two-slot ring, two workgroups per CU, measured
-// fastest: eight waves (two heads each) or a single workgroup with a deeper
-// ring lose more VALU efficiency than they gain in loads in flight.
+// K and V tile slots in its LDS ring (16 KB each; K tiles are loaded one
+// tile further ahead than V tiles), and how many such workgroups fit one CU
+// (80 KB of LDS each).  Four waves, two workgroups per CU measured fastest:
+// eight waves (two heads each), or three or four workgroups per CU with one
+// slot each, lose more VALU efficiency than they gain.
 constexpr int kGlobalWaves = 4;
-constexpr int kGlobalRing = 2;
-constexpr int kGlobalWGsPerCU = kGlobalRing <= 2 ? 2 : 1;
+constexpr int kGlobalKRing = 3;
+constexpr int kGlobalVRing = 2;
+constexpr int kGlobalWGsPerCU = 2;
 // Local-layer decode (latency-bound, one tile per workgroup): 8 waves of 2
 // heads put more waves behind each tile than 4 waves of 4 heads.
 constexpr int kLocalWaves = 8;

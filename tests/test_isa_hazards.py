@@ -1,8 +1,8 @@
 """Host check of the generated gfx950 code of the decode kernels.
 
-The query-key products are written as inline assembly (v_dot2c_f32_bf16 with
-a DPP row broadcast), which the compiler's hazard recognizer cannot see
-through.  Two rules are checked on the assembly of decode.hip (no GPU
+The query-key and weight-value products are written as inline assembly
+(v_dot2c_f32_bf16 with a DPP row broadcast), which the compiler's hazard
+recognizer cannot see through.  Two rules are checked on the assembly of decode.hip (no GPU
 needed), within each basic block:
   * the hardware requires two wait states between a VALU write of a VGPR
     and a DPP instruction reading it: none of a DPP product's VGPR operands
