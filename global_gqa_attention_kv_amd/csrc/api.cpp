@@ -83,7 +83,7 @@ BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify) {
                      : 0;
   p.part_bytes = p.splits > 1
                      ? align256((size_t)B * kHkv * p.qgroups * p.splits *
-                                p.qpw * kGroup * 132 * sizeof(float))
+                                p.qpw * kGroup * 68 * sizeof(float))
                      : 0;
   return p;
 }

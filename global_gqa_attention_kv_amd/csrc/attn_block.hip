@@ -55,7 +55,10 @@ constexpr int kTileB = kBlkTile * 256;      // one 64-key tile of K or V
 constexpr int kSlotB = 2 * kTileB;          // K tile, then V tile
 constexpr int kRing = 4;                    // tile slots in LDS (128 KB)
 constexpr int kWaves = kBlkQpw / 2;         // 8 waves of 32 rows
-constexpr int kPartRow = 132;               // floats: o[128], m, l, pad
+// Partial row of a key split, in 4-byte words: words 0..63 the row's output
+// over the split normalised by its own denominator (o / l) as 128 bf16,
+// word 64 the maximum m, word 65 the denominator l (fp32), 2 words padding.
+constexpr int kPartRow = 68;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
@@ -556,16 +559,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
     float* base = p.part +
                   ((((size_t)(b * kHkv + g) * p.qgroups + qg) * p.splits +
                     split) * ROWS + prow) * kPartRow;
+    // a row with no visible key in this split (l = 0) stores zeros
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    uint32_t* ob = reinterpret_cast<uint32_t*>(base);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
-        *reinterpret_cast<float4*>(base + 32 * d + 8 * ib + 4 * hi5) =
-            make_float4(O[d][4 * ib], O[d][4 * ib + 1], O[d][4 * ib + 2],
-                        O[d][4 * ib + 3]);
+        *reinterpret_cast<uint2*>(ob + (32 * d + 8 * ib + 4 * hi5) / 2) =
+            make_uint2(pack_bf16(O[d][4 * ib] * inv, O[d][4 * ib + 1] * inv),
+                       pack_bf16(O[d][4 * ib + 2] * inv,
+                                 O[d][4 * ib + 3] * inv));
     if (hi5 == 0) {
-      base[kD] = m_run;
-      base[kD + 1] = l_tot;
+      base[kD / 2] = m_run;
+      base[kD / 2 + 1] = l_tot;
     }
   } else {
     if (!row_valid) return;
@@ -591,11 +598,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
 }
 
 // Merge the key splits of one (sequence, token, query head, quarter of the
-// head dimension): 32 split lanes x 8 float4 columns per workgroup (thread =
-// 8 lane + column), every split's loads in flight at once.  The largest split
-// maximum M is found first, so the weighted sums need no rescaling and the
-// split lanes combine by plain addition:
-// o = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s.
+// head dimension): 32 split lanes x 8 columns of 4 dimensions per workgroup
+// (thread = 8 lane + column), every split's loads in flight at once.  The
+// largest split maximum M is found first, so the weighted sums need no
+// rescaling and the split lanes combine by plain addition; with the stored
+// o'_s = o_s / l_s, o = sum 2^(m_s - M) l_s o'_s / sum 2^(m_s - M) l_s.
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
   constexpr int ROWS = kBlkQpw * kGroup;
@@ -630,9 +637,11 @@ __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
     if (i >= nper) continue;
     const int s = sl + 32 * i;
     const float* ps = base + (size_t)min(s, p.splits - 1) * sstride;
-    ms[i] = s < p.splits ? ps[kD] : -INFINITY;
-    ls[i] = ps[kD + 1];
-    os[i] = *reinterpret_cast<const float4*>(ps + d);
+    ms[i] = s < p.splits ? ps[kD / 2] : -INFINITY;
+    ls[i] = ps[kD / 2 + 1];
+    const uint2 ob = *reinterpret_cast<const uint2*>(ps + d / 2);
+    os[i] = make_float4(bf16_lo(ob.x), bf16_hi(ob.x), bf16_lo(ob.y),
+                        bf16_hi(ob.y));
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -646,8 +655,8 @@ __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
   float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const float c = fast_exp2(ms[i] - M);
-    L += ls[i] * c;
+    const float c = fast_exp2(ms[i] - M) * ls[i];
+    L += c;
     O.x += os[i].x * c;
     O.y += os[i].y * c;
     O.z += os[i].z * c;
