@@ -597,17 +597,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
   }
 }
 
-// Merge the key splits of one (sequence, token, query head, quarter of the
-// head dimension): 32 split lanes x 8 columns of 4 dimensions per workgroup
-// (thread = 8 lane + column), every split's loads in flight at once.  The
+// Merge the key splits of one (sequence, token, query head): 32 split lanes
+// x 8 columns of 16 dimensions per workgroup (thread = 8 lane + column), so
+// the split rows are read whole, every split's loads in flight at once.  The
 // largest split maximum M is found first, so the weighted sums need no
 // rescaling and the split lanes combine by plain addition; with the stored
 // o'_s = o_s / l_s, o = sum 2^(m_s - M) l_s o'_s / sum 2^(m_s - M) l_s.
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
   constexpr int ROWS = kBlkQpw * kGroup;
-  const int dq = blockIdx.x & 3;
-  int rest = blockIdx.x >> 2;
+  int rest = blockIdx.x;
   const int h = rest % kHq;
   rest /= kHq;
   const int qi = rest % p.n;
@@ -620,28 +619,25 @@ __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
                 prow) * kPartRow;
   constexpr size_t sstride = (size_t)ROWS * kPartRow;
   const int tid = threadIdx.x;
-  const int c4 = tid & 7, sl = tid >> 3, w = tid >> 6;
-  const int d = dq * 32 + c4 * 4;
+  const int c = tid & 7, sl = tid >> 3, w = tid >> 6;
   __shared__ float wmax[4];
-  __shared__ float4 wsum[4][8];
-  __shared__ float wl[4][8];
+  __shared__ float wsum[4][8][17];
   constexpr int kPer = kMaxSplits / 32;  // the planner keeps splits <= 256
   float ms[kPer], ls[kPer];
-  float4 os[kPer];
+  uint4 os[kPer][2];  // dims 16c .. 16c + 15 as bf16
   const int nper = (p.splits + 31) / 32;  // batches holding a split
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     ms[i] = -INFINITY;
     ls[i] = 0.0f;
-    os[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    os[i][0] = os[i][1] = make_uint4(0, 0, 0, 0);
     if (i >= nper) continue;
     const int s = sl + 32 * i;
     const float* ps = base + (size_t)min(s, p.splits - 1) * sstride;
     ms[i] = s < p.splits ? ps[kD / 2] : -INFINITY;
     ls[i] = ps[kD / 2 + 1];
-    const uint2 ob = *reinterpret_cast<const uint2*>(ps + d / 2);
-    os[i] = make_float4(bf16_lo(ob.x), bf16_hi(ob.x), bf16_lo(ob.y),
-                        bf16_hi(ob.y));
+    os[i][0] = *reinterpret_cast<const uint4*>(ps + 8 * c);
+    os[i][1] = *reinterpret_cast<const uint4*>(ps + 8 * c + 4);
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -651,50 +647,54 @@ __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
   __syncthreads();
   const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   // splits without visible keys (m = -inf) and padding lanes weigh 0
-  float L = 0.0f;
-  float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float L = 0.0f, O[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) O[j] = 0.0f;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const float c = fast_exp2(ms[i] - M) * ls[i];
-    L += c;
-    O.x += os[i].x * c;
-    O.y += os[i].y * c;
-    O.z += os[i].z * c;
-    O.w += os[i].w * c;
+    const float cw = fast_exp2(ms[i] - M) * ls[i];
+    L += cw;
+    const uint32_t* wv = reinterpret_cast<const uint32_t*>(&os[i][0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      O[2 * j] += bf16_lo(wv[j]) * cw;
+      O[2 * j + 1] += bf16_hi(wv[j]) * cw;
+    }
   }
   // the 8 split lanes of a wave that share a column are 8 apart
 #pragma unroll
   for (int o = 8; o <= 32; o <<= 1) {
     L += __shfl_xor(L, o, 64);
-    O.x += __shfl_xor(O.x, o, 64);
-    O.y += __shfl_xor(O.y, o, 64);
-    O.z += __shfl_xor(O.z, o, 64);
-    O.w += __shfl_xor(O.w, o, 64);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) O[j] += __shfl_xor(O[j], o, 64);
   }
   if ((tid & 63) < 8) {
-    wsum[w][c4] = O;
-    wl[w][c4] = L;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) wsum[w][c][j] = O[j];
+    wsum[w][c][16] = L;
   }
   __syncthreads();
   if (tid >= 8) return;
-  float Lt = 0.0f;
-  float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float r[17];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    Lt += wl[j][c4];
-    r.x += wsum[j][c4].x;
-    r.y += wsum[j][c4].y;
-    r.z += wsum[j][c4].z;
-    r.w += wsum[j][c4].w;
-  }
-  const float inv = 1.0f / Lt;
-  const size_t o = (((size_t)b * p.n + qi) * kHq + h) * kD + d;
+  for (int j = 0; j < 17; ++j)
+    r[j] = wsum[0][c][j] + wsum[1][c][j] + wsum[2][c][j] + wsum[3][c][j];
+  const float inv = 1.0f / r[16];
+  const size_t o = (((size_t)b * p.n + qi) * kHq + h) * kD + 16 * c;
   if constexpr (OUT_F32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) =
-        make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + o);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dst[j] = make_float4(r[4 * j] * inv, r[4 * j + 1] * inv,
+                           r[4 * j + 2] * inv, r[4 * j + 3] * inv);
   } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(
-        pack_bf16(r.x * inv, r.y * inv), pack_bf16(r.z * inv, r.w * inv));
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + o);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dst[j] = make_uint4(pack_bf16(r[8 * j] * inv, r[8 * j + 1] * inv),
+                          pack_bf16(r[8 * j + 2] * inv, r[8 * j + 3] * inv),
+                          pack_bf16(r[8 * j + 4] * inv, r[8 * j + 5] * inv),
+                          pack_bf16(r[8 * j + 6] * inv, r[8 * j + 7] * inv));
   }
 }
 
@@ -708,7 +708,7 @@ hipError_t launch_main(const BlockParams& p, int B, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((block_merge_kernel<OUT_F32>),
-                       dim3(B * p.n * kHq * 4), dim3(256), 0, s, p);
+                       dim3(B * p.n * kHq), dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL((block_attn_kernel<LOCAL, false, OUT_F32>), grid, block,
                        0, s, p);
