@@ -70,10 +70,9 @@ BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify) {
   int64_t splits = 1;
   if (groups < kBlockTargetWGs)
     splits = (kBlockTargetWGs + groups - 1) / groups;
+  // down to one tile per workgroup (measured on the local verify: one tile
+  // per workgroup beat two now that split partials are bf16 rows)
   if (splits > tiles) splits = tiles;
-  // at least two tiles per workgroup: a split's fixed costs (Q load and
-  // rotation, ring fill, partial write) outweigh a single tile
-  if (splits > 1 && splits > tiles / 2) splits = tiles / 2 > 1 ? tiles / 2 : 1;
   if (splits < 1) splits = 1;
   p.splits = (int)splits;
   // local layers without key splits read pre-rotated keys from the
