@@ -188,6 +188,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
   const int qpos = pos0 + qic;
   const int klin0 = pos0 - (int)ring_prior(pos0);  // position of k_lin row 0
 
+  // Local layers: the sines and cosines of the workgroup's 16 tokens x 64
+  // frequencies, taken once (each thread one token and two frequencies) into
+  // the last ring slot, which no tile uses before the first step's barrier;
+  // the 16 lanes of a token (one per head) then read them instead of each
+  // evaluating its own.  Entry 32 t + j holds (sin, cos) of frequencies 2j
+  // and 2j + 1 at token q_first + t.
+  float4* const rtab = reinterpret_cast<float4*>(smem + (RING - 1) * kSlotB);
+  if constexpr (LOCAL) {
+    static_assert(WAVES * 64 == QPW * 32, "one table entry per thread");
+    const int t = tid >> 5, j = tid & 31;
+    const float tok = (float)min(q_first + t, q_last);
+    float r0 = tok * p.rope_rev[2 * j], r1 = tok * p.rope_rev[2 * j + 1];
+    r0 -= rintf(r0);
+    r1 -= rintf(r1);
+    float4 e;
+    sincos_rev(r0, &e.x, &e.y);
+    sincos_rev(r1, &e.z, &e.w);
+    rtab[tid] = e;
+    __syncthreads();
+  }
+
   // ---- Q^T operand: 8 k-steps of 16 dims, this lane's 8 dims of each
   bf16x8_t qreg[8];
   {
@@ -205,18 +226,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
     for (int k = 0; k < 4; ++k) {
       uint32_t* lo = reinterpret_cast<uint32_t*>(&raw[k]);
       uint32_t* hi = reinterpret_cast<uint32_t*>(&raw[k + 4]);
-      const float* rev = p.rope_rev + 16 * k + 8 * hi5;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x0 = bf16_lo(lo[e]), x1 = bf16_hi(lo[e]);
         float y0 = bf16_lo(hi[e]), y1 = bf16_hi(hi[e]);
         if (LOCAL) {
-          float r0 = (float)qic * rev[2 * e], r1 = (float)qic * rev[2 * e + 1];
-          r0 -= rintf(r0);
-          r1 -= rintf(r1);
-          float s0, c0, s1, c1;
-          sincos_rev(r0, &s0, &c0);
-          sincos_rev(r1, &s1, &c1);
+          // frequencies 16k + 8 hi5 + 2e and + 1 at this row's token
+          const float4 sc = rtab[32 * (qic - q_first) + 8 * k + 4 * hi5 + e];
+          const float s0 = sc.x, c0 = sc.y, s1 = sc.z, c1 = sc.w;
           const float a0 = x0 * c0 - y0 * s0, a1 = x1 * c1 - y1 * s1;
           const float b0 = y0 * c0 + x0 * s0, b1 = y1 * c1 + x1 * s1;
           x0 = a0, x1 = a1, y0 = b0, y1 = b1;
