@@ -328,15 +328,29 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
         read_batch(std::integral_constant<int, Bt + 1>{}, kbuf[(Bt + 1) & 1]);
       static_for<0, 4>([&](auto J) {
         constexpr int C = 4 * Bt + J;
-        static_for<0, 4>([&](auto I) {
-          constexpr int pr = 4 * C + I;
-          static_for<0, HW>([&](auto HL) {
-            constexpr int ii = I, bb = Bt & 1, jj = J, hh = HL;
-            acc[hh][ii % NACC] =
-                dot2_bf16_bcast<HL * LPH + pr / PPL, (C == 0 && ii < NACC)>(
-                    qv[pr % PPL], kbuf[bb][jj][ii], acc[hh][ii % NACC]);
+        constexpr int bb = Bt & 1, jj = J;
+        if constexpr (HW == 4) {
+          // pairs 4C .. 4C + 3 for the four heads in one asm block
+          const uint32_t qw[4] = {qv[(4 * C) % PPL], qv[(4 * C + 1) % PPL],
+                                  qv[(4 * C + 2) % PPL],
+                                  qv[(4 * C + 3) % PPL]};
+          const uint32_t kw[4] = {kbuf[bb][jj][0], kbuf[bb][jj][1],
+                                  kbuf[bb][jj][2], kbuf[bb][jj][3]};
+          float a4[4] = {acc[0][0], acc[1][0], acc[2][0], acc[3][0]};
+          dot2_bf16_bcast16<LPH, PPL, C, C == 0>(qw, kw, a4);
+          acc[0][0] = a4[0], acc[1][0] = a4[1], acc[2][0] = a4[2],
+          acc[3][0] = a4[3];
+        } else {
+          static_for<0, 4>([&](auto I) {
+            constexpr int pr = 4 * C + I;
+            static_for<0, HW>([&](auto HL) {
+              constexpr int ii = I, hh = HL;
+              acc[hh][ii % NACC] =
+                  dot2_bf16_bcast<HL * LPH + pr / PPL, (C == 0 && ii < NACC)>(
+                      qv[pr % PPL], kbuf[bb][jj][ii], acc[hh][ii % NACC]);
+            });
           });
-        });
+        }
       });
     });
     static_assert(HW * NACC == 4, "four score accumulators per wave");

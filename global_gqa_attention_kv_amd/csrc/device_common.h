@@ -27,6 +27,47 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // was last written four products earlier; the first product of each
 // accumulator (FIRST), whose accumulator was just initialised, carries its
 // own two wait states.  A host test checks the generated code.
+// The sixteen products of one 16-byte K chunk against four query heads, as
+// one asm block: for pair p = 0..3 of chunk C (k word k[p], query word q[p])
+// and head h, a[h] += dot2(q[p] broadcast from lane h LPH + (4C + p) / PPL of
+// the row, k[p]).  The compiler puts a wait state between consecutive asm
+// blocks (it cannot see what they hold), so fewer, larger blocks issue fewer
+// of them.  Inside the block a product's accumulator was written four
+// products earlier; FIRST adds two wait states for accumulators that were
+// just initialised.
+#define GQA_DOT1(A, Q, K, L)                                            \
+  "v_dot2c_f32_bf16_dpp %" #A ", %" #Q ", %" #K " row_newbcast:%" #L \
+  " row_mask:0xf bank_mask:0xf\n\t"
+#define GQA_DOT16                                                       \
+  GQA_DOT1(0, 4, 8, 12) GQA_DOT1(1, 4, 8, 13) GQA_DOT1(2, 4, 8, 14)   \
+  GQA_DOT1(3, 4, 8, 15) GQA_DOT1(0, 5, 9, 16) GQA_DOT1(1, 5, 9, 17)   \
+  GQA_DOT1(2, 5, 9, 18) GQA_DOT1(3, 5, 9, 19) GQA_DOT1(0, 6, 10, 20)  \
+  GQA_DOT1(1, 6, 10, 21) GQA_DOT1(2, 6, 10, 22) GQA_DOT1(3, 6, 10, 23) \
+  GQA_DOT1(0, 7, 11, 24) GQA_DOT1(1, 7, 11, 25) GQA_DOT1(2, 7, 11, 26) \
+  GQA_DOT1(3, 7, 11, 27)
+#define GQA_LANE(P, H) "i"((H) * LPH + (4 * C + (P)) / PPL)
+#define GQA_DOT16_OPERANDS                                              \
+  : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])                      \
+  : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(k[0]), "v"(k[1]),  \
+    "v"(k[2]), "v"(k[3]), GQA_LANE(0, 0), GQA_LANE(0, 1), GQA_LANE(0, 2), \
+    GQA_LANE(0, 3), GQA_LANE(1, 0), GQA_LANE(1, 1), GQA_LANE(1, 2),      \
+    GQA_LANE(1, 3), GQA_LANE(2, 0), GQA_LANE(2, 1), GQA_LANE(2, 2),      \
+    GQA_LANE(2, 3), GQA_LANE(3, 0), GQA_LANE(3, 1), GQA_LANE(3, 2),      \
+    GQA_LANE(3, 3)
+template <int LPH, int PPL, int C, bool FIRST>
+__device__ __forceinline__ void dot2_bf16_bcast16(const uint32_t (&q)[4],
+                                                  const uint32_t (&k)[4],
+                                                  float (&a)[4]) {
+  if constexpr (FIRST)
+    asm("s_nop 1\n\t" GQA_DOT16 GQA_DOT16_OPERANDS);
+  else
+    asm(GQA_DOT16 GQA_DOT16_OPERANDS);
+}
+#undef GQA_DOT16_OPERANDS
+#undef GQA_LANE
+#undef GQA_DOT16
+#undef GQA_DOT1
+
 template <int LANE, bool FIRST = false>
 __device__ __forceinline__ float dot2_bf16_bcast(uint32_t q, uint32_t k,
                                                  float acc) {
