@@ -35,8 +35,10 @@
 //    block's keys into the workspace once; queries are rotated when loaded.
 //    Both use offsets relative to p0 (<R_i q, R_j k> is unchanged by a common
 //    shift), keeping the fp32 angle arithmetic small.
-//  * Verification splits each sequence's key range across workgroups and
-//    merges the partial (m, l, o) rows in a second kernel.
+//  * Verification splits each sequence's key range across workgroups (down
+//    to one tile each) and merges the partial rows in a second kernel; a
+//    partial row is the split's output divided by its own denominator, as
+//    bf16, plus the maximum and the denominator in fp32.
 #include <type_traits>
 
 #include "device_common.h"
