@@ -361,6 +361,10 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill measurement and print "
                          "its JSON (for hardware-counter runs)")
+    ap.add_argument("--global-decode-calls", type=int, default=0,
+                    help="run only the global-layer decode call this many "
+                         "times over each of the 13 global layers and print "
+                         "its average (for hardware-counter runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB, "
                          "to scale hardware byte counters")
@@ -392,6 +396,12 @@ def main():
     torch.cuda.synchronize()
     print("# setup done: %d layers, batch %d, context %d" % (N_LAYERS, B, CTX),
           file=sys.stderr, flush=True)
+    if args.global_decode_calls:
+        kms = time_global_decode(ga, torch, layers, qs, outs, ws, positions,
+                                 kinds, args.global_decode_calls)
+        print(json.dumps({"global_decode_call_ms": round(kms, 5),
+                          "batch": B, "keys": pos + 1}), flush=True)
+        return
 
     ms, _graph = time_graph(torch, step, args.steps, args.warmup)
     check_step_outputs(ga, torch, layers, qs, outs, positions, kinds)
