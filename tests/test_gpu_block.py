@@ -90,6 +90,40 @@ def test_verify_full_size_131056(kind):
     check_close(out.cpu().numpy(), want, "verify 131056+16 kind=%d" % kind)
 
 
+@pytest.mark.parametrize("kind,needle", [
+    (ga.GLOBAL, 0), (ga.GLOBAL, 64 * 37 - 1), (ga.GLOBAL, 64 * 37),
+    (ga.GLOBAL, 131055), (ga.GLOBAL, 131056 + 3),
+    (ga.LOCAL, 131056 - 2047 + 5), (ga.LOCAL, 131056 - 2047 + 64 * 3),
+    (ga.LOCAL, 131055), (ga.LOCAL, 131056 + 9)])
+def test_verify_needle(kind, needle):
+    """A key far above the rest at a key-split boundary (splits are whole
+    64-key tiles), at the first or last prior key, inside the block (seen
+    only by the rows at or after it), or at the window edge of a local layer
+    (seen by the first rows only): every row must match the oracle, and on a
+    global layer every row that sees the needle must return its value."""
+    pos0, n = [131056], 16
+    k, v, u = si.needle_stream(si.seq_seed(1040, 0), pos0[0] + n, [needle],
+                               1041, magnitude=16.0)
+    cap = ga.MAX_CONTEXT if kind == ga.GLOBAL else None
+    layer = sentinel_cache(kind, 1, cap)
+    fill_layer(layer, [(k, v)], [pos0[0] - 1])
+    kb = k[pos0[0]:pos0[0] + n][None].contiguous()
+    vb = v[pos0[0]:pos0[0] + n][None].contiguous()
+    q = (u.float().repeat_interleave(16, dim=0) * 8.0).to(torch.bfloat16)
+    q = q[None, None].expand(1, n, ga.HQ, ga.D).contiguous()
+    print("verify needle kind=%d at %d" % (kind, needle), flush=True)
+    out = ga.attn_verify(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = _oracle_rows(kind, q, [(k, v)], pos0, list(range(n)))
+    check_close(got, want, "verify needle kind=%d at %d" % (kind, needle))
+    if kind == ga.GLOBAL:
+        target = np.repeat(v[needle].double().numpy(), 16, axis=0)
+        for r in range(n):
+            if pos0[0] + r >= needle:
+                assert np.abs(got[0, r] - target).max() < 0.05, r
+
+
 @pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
 def test_verify_rows_equal_decode_after_append(kind):
     """Verify token r == decode at pos0 + r once tokens 0..r are appended."""
