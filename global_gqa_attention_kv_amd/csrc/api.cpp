@@ -50,10 +50,10 @@ size_t decode_ws_bytes(int B, const DecodePlan& plan) {
                   sizeof(float));
 }
 
-// Block operations.  Verification (<= 16 tokens) uses 16-token workgroups
-// and splits the key range so about kBlockTargetWGs workgroups run; prefill
-// uses 8-token workgroups and splits keys only when the query groups alone
-// cannot fill the device.
+// Block operations.  Workgroups take 16 query tokens of one KV head; the
+// key range is split across workgroups (down to one 64-key tile each) only
+// when the query groups alone cannot fill the device with kBlockTargetWGs
+// workgroups: always for verification (<= 16 tokens), for short prefills.
 namespace {
 constexpr int kBlockTargetWGs = 256;
 }
