@@ -273,6 +273,7 @@ static int block_impl(const gqa_layer* layer, const void* q,
   p.n = n;
   p.qgroups = plan.qgroups;
   p.splits = plan.splits;
+  p.batch = B;
   p.scale_log2 = (float)(1.0 / sqrt((double)kD) * 1.4426950408889634);
   const bool local = layer->kind == GQA_LOCAL;
   if (local) {

@@ -160,9 +160,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
   const int hi5 = lane >> 5;
   const int row = lane & 31;
 
-  // workgroup -> (sequence, KV head, query group, key split); query groups
-  // with the longest key ranges are dispatched first
-  int bid = blockIdx.x;
+  // Work items are (sequence, KV head, query group, key split); with key
+  // splits a workgroup takes one item.  Without them (prefill) the grid is
+  // at most one workgroup per CU and each workgroup walks several items in
+  // snake order (w, 2G - 1 - w, 2G + w, ...), pairing a long key range with
+  // a short one, so no second dispatch round starts cold.  Items with the
+  // longest key ranges come first.
+  const int items = p.splits * p.qgroups * kHkv * p.batch;
+  const int G = gridDim.x;
+  const int walks = SPLIT ? 1 : (items + G - 1) / G;
+  for (int j = 0; j < walks; ++j) {
+  const int item = SPLIT ? (int)blockIdx.x
+                   : (j & 1) ? (j + 1) * G - 1 - (int)blockIdx.x
+                             : j * G + (int)blockIdx.x;
+  if (item >= items) break;  // uniform across the workgroup
+  if (j > 0) __syncthreads();  // the previous item's waves are done with LDS
+  int bid = item;
   const int split = bid % p.splits;
   bid /= p.splits;
   const int qg = p.qgroups - 1 - bid % p.qgroups;
@@ -593,8 +606,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
       base[kD / 2] = m_run;
       base[kD / 2 + 1] = l_tot;
     }
-  } else {
-    if (!row_valid) return;
+  } else if (row_valid) {
     const float inv = 1.0f / l_tot;
     const size_t obase = (((size_t)b * p.n + qi) * kHq + head) * kD;
 #pragma unroll
@@ -614,6 +626,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
         }
       }
   }
+  }  // work items
 }
 
 // Merge the key splits of one (sequence, token, query head): 32 split lanes
@@ -719,7 +732,10 @@ __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
 
 template <bool LOCAL, bool OUT_F32>
 hipError_t launch_main(const BlockParams& p, int B, hipStream_t s) {
-  const dim3 grid(p.splits * p.qgroups * kHkv * B);
+  const int items = p.splits * p.qgroups * kHkv * B;
+  // without key splits: at most one workgroup per CU, each walking its items
+  const int walks = p.splits > 1 ? 1 : (items + kCUs - 1) / kCUs;
+  const dim3 grid((items + walks - 1) / walks);
   const dim3 block(kWaves * 64);
   if (p.splits > 1) {
     hipLaunchKernelGGL((block_attn_kernel<LOCAL, true, OUT_F32>), grid, block,

@@ -97,6 +97,7 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
 // few thousand, bf16 output) and speculative verification (n <= 16, fp32
 // output, keys split across workgroups).
 constexpr int kBlkTile = 64;               // keys per tile
+constexpr int kCUs = 256;                  // compute units of an MI355X
 constexpr int kBlkQpw = 16;                // query tokens per workgroup
 constexpr int kMaxPrefill = GQA_MAX_CONTEXT;
 
@@ -124,7 +125,7 @@ struct BlockParams {
   int32_t n;
   int32_t qgroups;
   int32_t splits;
-  int32_t pad_;
+  int32_t batch;            // B
   float scale_log2;
   float rope_rev[kD / 2];
   int64_t pos0[kMaxBatch];
