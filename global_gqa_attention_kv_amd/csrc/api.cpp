@@ -58,7 +58,7 @@ namespace {
 constexpr int kBlockTargetWGs = 256;
 }
 
-BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify) {
+BlockPlan plan_block(int kind, int B, int n, int64_t max_keys) {
   BlockPlan p;
   p.qpw = kBlkQpw;
   p.qgroups = (n + p.qpw - 1) / p.qpw;
@@ -128,7 +128,7 @@ size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx) {
       const bool verify = op == GQA_OP_VERIFY;
       if (n > (verify ? GQA_MAX_VERIFY : GQA_MAX_CONTEXT)) return 0;
       const int64_t keys = visible_keys(kind, max_ctx - 1);
-      return block_ws_bytes(plan_block(kind, B, n, keys, verify));
+      return block_ws_bytes(plan_block(kind, B, n, keys));
     }
     default:
       return 0;
@@ -251,7 +251,7 @@ static int block_impl(const gqa_layer* layer, const void* q,
   int rc = check_block(layer, q, k_blk, v_blk, pos0, B, n, out, verify,
                        &max_keys);
   if (rc != GQA_OK) return rc;
-  const BlockPlan plan = plan_block(layer->kind, B, n, max_keys, verify);
+  const BlockPlan plan = plan_block(layer->kind, B, n, max_keys);
   if (!ws) return GQA_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
   if (ws_bytes < block_ws_bytes(plan)) return GQA_ERR_WS_TOO_SMALL;

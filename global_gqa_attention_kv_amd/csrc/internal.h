@@ -108,7 +108,7 @@ struct BlockPlan {
   size_t klin_bytes;   // local: pre-rotated keys
   size_t part_bytes;   // split partials
 };
-BlockPlan plan_block(int kind, int B, int n, int64_t max_keys, bool verify);
+BlockPlan plan_block(int kind, int B, int n, int64_t max_keys);
 size_t block_ws_bytes(const BlockPlan& plan);
 
 struct BlockParams {
