@@ -17,6 +17,9 @@ What it defines, each cited by page and section:
 * :func:`merge` -- recombining partial sums over disjoint key sets (the
   log-sum-exp identity; the pages only require that the result is the plain
   one, "memory-efficient kernels" in "Long context still costs compute").
+* :func:`attend_block_together` -- a block of tokens predicted together
+  (block-diffusion drafting, section 04 of the shishifenxi.com page): every
+  query of the block sees the context and the whole block.
 * :func:`expected_cache` -- integer-only cache contents after a sequence of
   appends: global slot = position, local slot = position mod window, latest
   write wins ("Narrow cache": the engine must evict or cyclically reuse stale
@@ -197,6 +200,31 @@ def merge(parts):
     L = sum(w[i] * parts[i][1] for i in range(len(parts)))
     O = sum(w[i][..., None] * parts[i][2] for i in range(len(parts)))
     return O / L[..., None]
+
+
+def attend_block_together(q, pos0, k, v, kpos0, *, hq, hkv, d, nthreads=None):
+    """Attention of a block of n tokens at positions pos0 .. pos0+n-1 that are
+    predicted together, as in a block-diffusion drafter's step (page "Deep
+    dive into Muse Glimmer", shishifenxi.com, section 04: the drafter
+    predicts a 16-token block in parallel rather than token by token, and the
+    target's hidden features from five layers enter every drafter layer's
+    keys and values).  With no order inside the block, every query of the
+    block sees every key at positions 0 .. pos0+n-1: the context before the
+    block and the whole block.  Only for layers without RoPE and without a
+    window (the pages give the drafter neither).
+
+    On such a layer a query's position enters the result only through its
+    visible set, and the set {j <= pos0+n-1} is the causal set of position
+    pos0+n-1; so each row is the plain attention of that query placed at the
+    block's last position, which :func:`attend` computes.
+
+    q: [n, hq, d] bf16 bits; k, v: [nk, hkv, d] bf16 bits, row r at position
+    kpos0 + r, covering 0 .. pos0+n-1.  Returns float64 [n, hq, d]."""
+    q = _bits(q).reshape(-1, hq, d)
+    n = q.shape[0]
+    see = np.full(n, int(pos0) + n - 1, dtype=np.int64)
+    return attend(q, see, k, v, kpos0, hq=hq, hkv=hkv, d=d, window=0,
+                  rope=False, nthreads=nthreads)
 
 
 def rope(x, t, theta=10000.0):
