@@ -212,6 +212,12 @@ def pairs_block(kind, pos0, n, window=2048):
     return total
 
 
+def pairs_block_together(pos0, n):
+    """Pairs of a block of n tokens at pos0 predicted together: every token
+    sees positions 0 .. pos0+n-1."""
+    return n * (pos0 + n)
+
+
 def bench_verify(ga, torch, layers, kinds, B, reps=5, seed=4004):
     """52-layer verification of a 16-token drafted block at 131056..131071
     over the caches of the decode step (their first 131056 positions serve as
@@ -252,6 +258,45 @@ def bench_verify(ga, torch, layers, kinds, B, reps=5, seed=4004):
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
             "workload": "52-layer verify, 16 drafted tokens at 131056..131071, "
                         "batch %d" % B}
+
+
+def bench_draft(ga, torch, layers, kinds, B, n_drafter=5, reps=5, seed=4404):
+    """A 5-layer drafter's attention over a 16-token block predicted together
+    at 131056..131071 (every block token sees the context and the whole
+    block).  The first five global caches of the decode step stand in for
+    the drafter's context keys and values.  Returns a dict of figures."""
+    dev = torch.device("cuda")
+    n, pos0 = 16, CTX - 16
+    glob = [l for l in range(N_LAYERS) if kinds[l] == ga.GLOBAL][:n_drafter]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    blk = []
+    for _ in glob:
+        q = torch.randn((B, n, ga.HQ, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        kb = torch.randn((B, n, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        vb = torch.randn((B, n, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        blk.append((q, kb, vb))
+    ws = torch.empty(ga.workspace_bytes(ga.OP_DRAFT, ga.GLOBAL, B, n, CTX),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((B, n, ga.HQ, ga.D), dtype=torch.float32, device=dev)
+    positions = [pos0] * B
+
+    def step():
+        for i, l in enumerate(glob):
+            q, kb, vb = blk[i]
+            ga.attn_draft_block(layers[l], q, kb, vb, positions, out, ws)
+
+    ms, _ = time_graph(torch, step, reps, 2)
+    flops = len(glob) * B * pairs_block_together(pos0, n) * 4 * ga.HQ * ga.D
+    kvb = len(glob) * B * CTX * 1024
+    return {"ms_per_step": round(ms, 4),
+            "kv_GBps": round(kvb / (ms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(kvb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "workload": "%d drafter layers, a 16-token block predicted "
+                        "together at 131056..131071 over a 131056-token "
+                        "context, batch %d" % (len(glob), B)}
 
 
 def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005):
@@ -457,6 +502,8 @@ def main():
     if not args.no_extras:
         line["verify"] = bench_verify(ga, torch, layers, kinds, 1)
         print("# verify done", file=sys.stderr, flush=True)
+        line["draft_block"] = bench_draft(ga, torch, layers, kinds, 1)
+        print("# drafted block done", file=sys.stderr, flush=True)
         del layers, qs, outs, ws, step
         torch.cuda.empty_cache()
         line["decode_b1"] = bench_decode_b1(ga, torch, args.steps, args.warmup)

@@ -18,8 +18,8 @@ import os
 import torch
 
 __all__ = [
-    "LOCAL", "GLOBAL", "OP_DECODE", "OP_VERIFY", "OP_PREFILL", "MAX_VERIFY",
-    "attn_verify", "attn_prefill", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
+    "LOCAL", "GLOBAL", "OP_DECODE", "OP_VERIFY", "OP_PREFILL", "OP_DRAFT",
+    "MAX_VERIFY", "attn_verify", "attn_draft_block", "attn_prefill", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
     "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
     "attn_decode", "attn_decode_append", "attn_decode_dev", "workspace_bytes", "workspace", "status_string", "abi_version",
     "library_path", "layer_kind",
@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libgqa_attn.so")
 
 LOCAL, GLOBAL = 0, 1
-OP_DECODE, OP_VERIFY, OP_PREFILL = 0, 1, 2
+OP_DECODE, OP_VERIFY, OP_PREFILL, OP_DRAFT = 0, 1, 2, 3
 MAX_VERIFY = 16
 HQ, HKV, D, WINDOW, MAX_CONTEXT, MAX_BATCH = 32, 2, 128, 2048, 131072, 64
 ROPE_THETA = 10000.0
@@ -81,6 +81,9 @@ def _load():
         lib.gqa_attn_verify.restype = i32
         lib.gqa_attn_verify.argtypes = [L, p, p, p, p, i32, i32, p, p,
                                         ctypes.c_size_t, p]
+        lib.gqa_attn_draft_block.restype = i32
+        lib.gqa_attn_draft_block.argtypes = [L, p, p, p, p, i32, i32, p, p,
+                                             ctypes.c_size_t, p]
         lib.gqa_attn_prefill.restype = i32
         lib.gqa_attn_prefill.argtypes = [L, p, p, p, p, i32, i32, p, p,
                                          ctypes.c_size_t, p]
@@ -309,6 +312,18 @@ def attn_verify(layer: Layer, q, k_blk, v_blk, pos0, out=None, ws=None,
     cache).  Returns fp32 [B, n, 32, 128].  The cache is not modified."""
     return _block_common(_load().gqa_attn_verify, "gqa_attn_verify",
                          OP_VERIFY, torch.float32, layer, q, k_blk, v_blk,
+                         pos0, out, ws, stream)
+
+
+def attn_draft_block(layer: Layer, q, k_blk, v_blk, pos0, out=None, ws=None,
+                     stream=None):
+    """Attention of a drafted block predicted together (one block-diffusion
+    drafting step): q bf16 [B, n, 32, 128] (n <= 16) at positions pos0[b] ..
+    pos0[b]+n-1, k_blk, v_blk bf16 [B, n, 2, 128] (not in the cache); every
+    block token sees the cached context and the whole block.  Global layers
+    only.  Returns fp32 [B, n, 32, 128]; the cache is not modified."""
+    return _block_common(_load().gqa_attn_draft_block, "gqa_attn_draft_block",
+                         OP_DRAFT, torch.float32, layer, q, k_blk, v_blk,
                          pos0, out, ws, stream)
 
 

@@ -123,9 +123,12 @@ size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx) {
       const int64_t keys = visible_keys(kind, max_ctx - 1);
       return decode_ws_bytes(B, plan_decode(kind, B, keys));
     }
+    case GQA_OP_DRAFT:
+      if (kind != GQA_GLOBAL) return 0;
+      [[fallthrough]];
     case GQA_OP_VERIFY:
     case GQA_OP_PREFILL: {
-      const bool verify = op == GQA_OP_VERIFY;
+      const bool verify = op != GQA_OP_PREFILL;
       if (n > (verify ? GQA_MAX_VERIFY : GQA_MAX_CONTEXT)) return 0;
       const int64_t keys = visible_keys(kind, max_ctx - 1);
       return block_ws_bytes(plan_block(kind, B, n, keys));
@@ -246,11 +249,13 @@ int gqa_attn_decode_dev(const gqa_layer* layer, const void* q,
 static int block_impl(const gqa_layer* layer, const void* q,
                       const void* k_blk, const void* v_blk,
                       const int64_t* pos0, int B, int n, void* out, void* ws,
-                      size_t ws_bytes, bool verify, void* stream) {
+                      size_t ws_bytes, bool verify, bool together,
+                      void* stream) {
   int64_t max_keys = 0;
   int rc = check_block(layer, q, k_blk, v_blk, pos0, B, n, out, verify,
                        &max_keys);
   if (rc != GQA_OK) return rc;
+  if (together && layer->kind != GQA_GLOBAL) return GQA_ERR_UNSUPPORTED;
   const BlockPlan plan = plan_block(layer->kind, B, n, max_keys);
   if (!ws) return GQA_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
@@ -274,6 +279,7 @@ static int block_impl(const gqa_layer* layer, const void* q,
   p.qgroups = plan.qgroups;
   p.splits = plan.splits;
   p.batch = B;
+  p.together = together ? 1 : 0;
   p.scale_log2 = (float)(1.0 / sqrt((double)kD) * 1.4426950408889634);
   const bool local = layer->kind == GQA_LOCAL;
   if (local) {
@@ -290,7 +296,15 @@ int gqa_attn_verify(const gqa_layer* layer, const void* q, const void* k_blk,
                     const void* v_blk, const int64_t* pos0, int B, int n,
                     float* out, void* ws, size_t ws_bytes, void* stream) {
   return block_impl(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
-                    true, stream);
+                    true, false, stream);
+}
+
+int gqa_attn_draft_block(const gqa_layer* layer, const void* q,
+                         const void* k_blk, const void* v_blk,
+                         const int64_t* pos0, int B, int n, float* out,
+                         void* ws, size_t ws_bytes, void* stream) {
+  return block_impl(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
+                    true, true, stream);
 }
 
 int gqa_attn_prefill(const gqa_layer* layer, const void* q,
@@ -298,7 +312,7 @@ int gqa_attn_prefill(const gqa_layer* layer, const void* q,
                      const int64_t* pos0, int B, int n, void* out, void* ws,
                      size_t ws_bytes, void* stream) {
   return block_impl(layer, q, k_chunk, v_chunk, pos0, B, n, out, ws,
-                    ws_bytes, false, stream);
+                    ws_bytes, false, false, stream);
 }
 
 }  // extern "C"

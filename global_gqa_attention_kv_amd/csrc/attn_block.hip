@@ -13,6 +13,10 @@
 // Muse Glimmer" (shishifenxi.com) section 04 and "Meta open-sources the 30B
 // Muse Glimmer" (kongchang.com), "Trick 3: D-Flash" (a 16-token drafted
 // block verified by the main model in one pass, causal within the block).
+// A block can also be taken as predicted together, as a block-diffusion
+// drafter does (shishifenxi.com section 04): then every query of the block
+// sees the whole block (global layers only, where a query's position
+// matters only through the keys it sees).
 //
 // Design (gfx950, v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //  * Rows are (query, head) pairs: a workgroup takes 16 query tokens x the
@@ -188,8 +192,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
   const int q_first = qg * QPW;
   const int q_last = min(p.n - 1, q_first + QPW - 1);
   const int i_first = pos0 + q_first, i_last = pos0 + q_last;
+  // Last key position each query of the group sees: its own (causal inside
+  // the block), or the block's last one when the block's tokens are
+  // predicted together (no order inside the block; layers without RoPE).
+  const int blk_last = pos0 + p.n - 1;
+  const int see_first = p.together ? blk_last : i_first;
   const int k_lo = LOCAL ? max(0, i_first - (kW - 1)) : 0;
-  const int k_hi = i_last + 1;
+  const int k_hi = (p.together ? blk_last : i_last) + 1;
   const int tiles_all = (k_hi - k_lo + kBlkTile - 1) / kBlkTile;
   const int tps = (tiles_all + p.splits - 1) / p.splits;
   const int t_begin = split * tps;
@@ -201,6 +210,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
   const int qic = min(qi, q_last);
   const int head = g * kGroup + (row & 15);
   const int qpos = pos0 + qic;
+  const int qsee = p.together ? blk_last : qpos;
   const int klin0 = pos0 - (int)ring_prior(pos0);  // position of k_lin row 0
 
   // Local layers: the sines and cosines of the workgroup's 16 tokens x 64
@@ -432,12 +442,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
     // ---- softmax update for this lane's row.  The maximum is taken on raw
     // scores, already scaled to log2 units and shifted by -mb: p = 2^(S).
     const int kb = k_lo + (t_begin + t) * kBlkTile;
-    const bool edge = (kb + kBlkTile - 1 > i_first) ||
+    const bool edge = (kb + kBlkTile - 1 > see_first) ||
                       (LOCAL && kb <= i_last - kW);
     if (edge) {
       // key kb + off + 4 hi5 is visible iff off <= rel and (local)
       // off > rel - W
-      const int rel = qpos - kb - 4 * hi5;
+      const int rel = qsee - kb - 4 * hi5;
 #pragma unroll
       for (int be = 0; be < 2; ++be)
 #pragma unroll

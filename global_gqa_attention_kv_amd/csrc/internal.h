@@ -94,8 +94,10 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
 // ---------------------------------------------------------------- block
 // A block of n query tokens per sequence at positions pos0 .. pos0+n-1 whose
 // K/V (k_blk, v_blk) are not in the cache yet: chunked prefill (n up to a
-// few thousand, bf16 output) and speculative verification (n <= 16, fp32
-// output, keys split across workgroups).
+// few thousand, bf16 output), speculative verification (n <= 16, fp32
+// output, keys split across workgroups) and a drafted block whose tokens
+// are predicted together (as verification, without the causal order inside
+// the block).
 constexpr int kBlkTile = 64;               // keys per tile
 constexpr int kCUs = 256;                  // compute units of an MI355X
 constexpr int kBlkQpw = 16;                // query tokens per workgroup
@@ -126,6 +128,7 @@ struct BlockParams {
   int32_t qgroups;
   int32_t splits;
   int32_t batch;            // B
+  int32_t together;         // 1: every query sees the whole block (global)
   float scale_log2;
   float rope_rev[kD / 2];
   int64_t pos0[kMaxBatch];

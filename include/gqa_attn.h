@@ -65,6 +65,7 @@ extern "C" {
 #define GQA_OP_DECODE 0
 #define GQA_OP_VERIFY 1
 #define GQA_OP_PREFILL 2
+#define GQA_OP_DRAFT 3
 
 /* Status codes. */
 #define GQA_OK 0
@@ -167,6 +168,25 @@ int gqa_attn_decode_dev(const gqa_layer* layer, const void* q,
 int gqa_attn_verify(const gqa_layer* layer, const void* q, const void* k_blk,
                     const void* v_blk, const int64_t* pos0, int B, int n,
                     float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Attention of a drafted block whose n (1..GQA_MAX_VERIFY) tokens at
+ * positions pos0[b] .. pos0[b]+n-1 are predicted together, as in one step of
+ * a block-diffusion drafter: every token of the block attends to the cached
+ * positions 0 .. pos0[b]-1 and to ALL n block tokens (no causal order inside
+ * the block).  Global layers only (GQA_GLOBAL: no RoPE, no window); a local
+ * layer returns GQA_ERR_UNSUPPORTED.  Arguments, layouts (q [B][n][32][128]
+ * bf16, k_blk / v_blk [B][n][2][128] bf16 not in the cache, out
+ * [B][n][32][128] fp32), ownership and errors as gqa_attn_verify; ws must
+ * hold gqa_workspace_bytes(GQA_OP_DRAFT, GQA_GLOBAL, B, n, max pos0 + n)
+ * bytes.  The cache is not touched.
+ * Pages: shishifenxi.com section 04 (the drafter predicts a 16-token block
+ * in parallel by block diffusion instead of token by token, and the target's
+ * hidden features from five of its layers enter every drafter layer's keys
+ * and values -- here: the cached context). */
+int gqa_attn_draft_block(const gqa_layer* layer, const void* q,
+                         const void* k_blk, const void* v_blk,
+                         const int64_t* pos0, int B, int n, float* out,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* Chunked prefill: n (1..GQA_MAX_CONTEXT) prompt tokens per sequence at
  * positions pos0[b] .. pos0[b]+n-1.  Same visibility rules and arguments as

@@ -195,7 +195,8 @@ def test_decode_dev_validation(lib):
     assert call(max_pos=4095, ws_bytes=need - 1) == E_WS
 
 
-@pytest.mark.parametrize("fn", ["gqa_attn_verify", "gqa_attn_prefill"])
+@pytest.mark.parametrize("fn", ["gqa_attn_verify", "gqa_attn_draft_block",
+                                "gqa_attn_prefill"])
 def test_block_validation(lib, fn):
     f = getattr(lib, fn)
     L = _layer()
@@ -212,7 +213,7 @@ def test_block_validation(lib, fn):
     assert call(n=0) == E_ARG
     assert call(B=0) == E_ARG
     assert call(ws=None) == E_ARG
-    if fn == "gqa_attn_verify":
+    if fn != "gqa_attn_prefill":
         assert call(n=17) == E_ARG                      # block of at most 16
     else:
         assert call(n=17, pos=_pos(0), ws_bytes=0) == E_WS
@@ -221,10 +222,16 @@ def test_block_validation(lib, fn):
     assert call(ws=FAKE + 64) == E_ALN
     assert call(pos=_pos(4096 - 15)) == E_POS           # pos0 + n > capacity
     assert call(pos=_pos(-1)) == E_POS
-    need = ga.workspace_bytes(ga.OP_VERIFY if fn == "gqa_attn_verify"
-                              else ga.OP_PREFILL, ga.GLOBAL, 1, 16, 4096)
+    op = {"gqa_attn_verify": ga.OP_VERIFY, "gqa_attn_draft_block": ga.OP_DRAFT,
+          "gqa_attn_prefill": ga.OP_PREFILL}[fn]
+    need = ga.workspace_bytes(op, ga.GLOBAL, 1, 16, 4096)
     assert need > 0
     assert call(pos=_pos(4080), ws_bytes=need - 1) == E_WS
+    if fn == "gqa_attn_draft_block":
+        # a block predicted together is defined on global layers only
+        assert ga.workspace_bytes(op, ga.LOCAL, 1, 16, 4096) == 0
+        assert call(layer=_layer(kind=ga.LOCAL)) == E_UNS
+        assert need == ga.workspace_bytes(ga.OP_VERIFY, ga.GLOBAL, 1, 16, 4096)
     # local layers need room for the rotated window in the workspace
     loc = ga.workspace_bytes(ga.OP_PREFILL, ga.LOCAL, 1, 4096, 131072)
     assert loc >= (2048 + 4096) * 512

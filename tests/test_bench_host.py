@@ -45,6 +45,15 @@ def test_verify_pairs():
     assert bench.pairs_block(LOCAL, 131056, 16) == 16 * 2048
 
 
+def test_block_together_pairs():
+    # every one of the 16 tokens sees the 131056 context keys and all 16
+    assert bench.pairs_block_together(131056, 16) == 16 * 131072
+    assert bench.pairs_block_together(0, 1) == 1
+    # the causal block's last token sees as many as any token here
+    assert bench.pairs_block_together(131056, 16) >= bench.pairs_block(
+        GLOBAL, 131056, 16)
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
                         "--gpus", "2"], capture_output=True, text=True,
