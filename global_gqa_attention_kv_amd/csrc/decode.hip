@@ -11,19 +11,23 @@
 // Design (gfx950, VALU; decode is a streaming read of the cache):
 //  * A workgroup owns one (sequence, KV head, key split) and serves all 16
 //    query heads of that KV head out of the same tiles, so each cached K/V
-//    byte is fetched from HBM once.  Global layers: 4 waves of 4 heads, two
-//    workgroups per CU, long splits; local layers (a 2048-key window, so
-//    latency rather than bandwidth): 8 waves of 2 heads, one 64-key tile per
-//    workgroup up to batch 4.
+//    byte is fetched from HBM once.  Global layers: 4 waves, two workgroups
+//    per CU, long splits; each wave takes the 16 keys of every tile whose
+//    rows it loads itself, for all 16 heads, so the waves never wait for one
+//    another inside the tile loop and merge their sums once at the end.
+//    Local layers (a 2048-key window, so latency rather than bandwidth): 8
+//    waves of 2 heads over the whole tile, one 64-key tile per workgroup up
+//    to batch 4.
 //  * Tiles of 64 keys go straight from HBM into LDS rings with direct-to-LDS
 //    loads (global_load_lds_dwordx4: lane l's 16 bytes land at the wave's LDS
 //    base + 16 l, never passing through VGPRs), marked non-temporal since the
 //    cache is streamed once per step.  K and V tiles have rings of their own;
 //    on global layers K tiles are loaded two tiles ahead and V tiles one
 //    (three K slots, two V slots: 80 KB, two workgroups per CU).
-//  * Q.K: lane = key; the query words are wave-uniform, held 16 to a VGPR
-//    and broadcast with DPP row_newbcast into v_dot2c_f32_bf16 (bf16
-//    products exact, fp32 accumulation).  K rows sit in LDS with 16-byte
+//  * Q.K: lane = key (global layers: lane 16 r + j = key j of the wave's 16,
+//    heads 4 r .. 4 r + 3); the query words are uniform across each 16-lane
+//    row, held 16 to a VGPR and broadcast with DPP row_newbcast into
+//    v_dot2c_f32_bf16 (bf16 products exact, fp32 accumulation).  K rows sit in LDS with 16-byte
 //    chunk c of row r at chunk slot c ^ (r & 15), so a lane reads its whole
 //    row without bank conflicts.
 //  * Local layers rotate each landed K tile in LDS by its keys' offsets to
@@ -103,6 +107,18 @@ __device__ __forceinline__ void dma16(const uint16_t* base, uint32_t off,
       : "v"(off), "s"(base), "s"(lds)
       : "memory");
 }
+// Maximum and sum over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row_max(float x) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 16));
+  return x;
+}
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) x += __shfl_xor(x, o, 16);
+  return x;
+}
+
 // s_waitcnt vmcnt(N): at most N of this wave's vector memory operations
 // (here: ring loads) still outstanding.
 template <int N>
@@ -116,7 +132,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // one tile further ahead).  LOCAL: the keys are the window
 // max(0, pos - 2047) .. pos read through the ring, and each landed K tile is
 // rotated in LDS by its keys' offsets to the query before the products.
-template <int WAVES, int HPW, int KR, int VR, bool LOCAL>
+// KSPLIT: the waves split every tile's keys instead of the heads -- wave w
+// takes the 16 keys whose rows it loads itself, for all 16 heads (row r of
+// the wave: heads 4 r .. 4 r + 3) -- so no wave reads another's rows and
+// the tile loop needs no barrier; the four waves' sums are combined once at
+// the end.
+template <int WAVES, int HPW, int KR, int VR, bool LOCAL, bool KSPLIT = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     const DecodeParams p) {
   constexpr int NT = 64 * WAVES;
@@ -129,6 +150,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   constexpr int LPT = RPW / 4;            // loads per K (or V) tile per wave
   static_assert(HW == 2 || HW == 4, "two or four heads per wave");
   static_assert(KR == VR || KR == VR + 1, "K at most one tile further ahead");
+  static_assert(!KSPLIT || (!LOCAL && WAVES == 4 && HPW == kGroup && KR > 1),
+                "key split: global layers, four waves of 16 keys, all heads");
   __shared__ __attribute__((aligned(16))) uint8_t smem[(KR + VR) * kTileBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,7 +222,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   const uint16_t* Vb = p.v + (int64_t)b * p.seq_stride + g * kD;
   const uint16_t* Kn = p.k_new + (int64_t)b * kTokenElems + g * kD;
   const uint16_t* Vn = p.v_new + (int64_t)b * kTokenElems + g * kD;
-  const int head0 = g * kGroup + hg * HPW + w * HW;
+  // first head of this lane's row: the wave's heads, or (KSPLIT) row r's
+  const int hrow = KSPLIT ? (lane >> 4) * HW : w * HW;  // within the group
+  const int head0 = g * kGroup + hg * HPW + hrow;
 
   // The wave's HW query rows (64 bf16 pairs each) held as wave-uniform words
   // for the DPP broadcast: within every 16-lane row, lane n keeps pairs
@@ -280,7 +305,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   float m[HW], lsum[HW], o[HW][8];
 #pragma unroll
   for (int hl = 0; hl < HW; ++hl) {
-    m[hl] = -INFINITY;
+    // KSPLIT: a wave may see no valid key in its first tiles; a finite
+    // floor keeps 2^(s - m) at 0 there instead of 2^(-inf + inf)
+    m[hl] = KSPLIT ? -1e30f : -INFINITY;
     lsum[hl] = 0.0f;
     // each accumulator gets a register of its own (a shared zero would be
     // copied in right before the first DPP product that reads it)
@@ -288,23 +315,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     for (int e = 0; e < 8; ++e) asm volatile("v_mov_b32 %0, 0" : "=v"(o[hl][e]));
   }
 
-  // LDS read offsets: the K row of key = lane, and the P.V transposes: row
-  // kg of the wave (lanes 16 kg ..) reads keys 16 kg + 4 q + (j >> 2), dims
+  // LDS read offsets: the K row of key = lane (KSPLIT: 16 w + lane % 16),
+  // and the P.V transposes: row kg of the wave (lanes 16 kg ..) reads keys
+  // 16 kg + 4 q + (j >> 2) (KSPLIT: 16 w + 4 q + (j >> 2) in every row), dims
   // 16 e + 4 (j & 3) for key quad q of its row; for odd q the swizzle puts
   // dims 16 e at the offset of dims 16 (e ^ 4) of q = 0.
   const int kg = lane >> 4, jl = lane & 15, ja = jl & 3, je = jl >> 2;
   uint32_t krd[16], vrd[8];
+  // KSPLIT: key 16 w + jl in the products, V rows 16 w .. of every row
+  const int krow = KSPLIT ? 16 * w + jl : lane;
+  const int vgrp = KSPLIT ? w : kg;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) krd[c] = lds_base + lane * 256 + ((c ^ jl) << 4);
+  for (int c = 0; c < 16; ++c) krd[c] = lds_base + krow * 256 + ((c ^ jl) << 4);
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    vrd[e] = vbase + (16 * kg + je) * 256 + 32 * (e ^ je) + 8 * ja;
+    vrd[e] = vbase + (16 * vgrp + je) * 256 + 32 * (e ^ je) + 8 * ja;
 
   auto consume = [&](int t, auto KS, auto VS) {
     constexpr uint32_t so = KS * kTileBytes;
     constexpr uint32_t vso = VS * kTileBytes;
-    // ---- scores: lane = key of this tile; the query word of (head hl,
-    // pair pr) is broadcast from lane hl * LPH + pr / PPL.  The lane's K row
+    // ---- scores: lane = key of this tile (KSPLIT: key krow); the query
+    // word of (head hl, pair pr) is broadcast from lane hl * LPH + pr / PPL
+    // of the lane's row.  The lane's K row
     // is read from LDS in 4 batches of 64 B, one batch ahead of the
     // products; consecutive products alternate between accumulators, so a
     // product's accumulator was last written four instructions earlier (a
@@ -368,7 +400,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     read_quad(std::integral_constant<int, 0>{}, vw[0]);
     dpp_settle(acc[0][0], acc[(1 / NACC) % HW][1 % NACC],
                acc[(2 / NACC) % HW][2 % NACC], acc[(3 / NACC) % HW][3 % NACC]);
-    const bool valid = k_begin + t * kDecTile + lane < k_end;
+    const bool valid = k_begin + t * kDecTile + krow < k_end;
     float s2[HW];
     bool need = false;
 #pragma unroll
@@ -382,7 +414,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     if (__any(need)) {
 #pragma unroll
       for (int hl = 0; hl < HW; ++hl) {
-        const float mn = fmaxf(m[hl], wave_max(s2[hl]));
+        const float mn =
+            fmaxf(m[hl], KSPLIT ? row_max(s2[hl]) : wave_max(s2[hl]));
         const float alpha = fast_exp2(m[hl] - mn);
         m[hl] = mn;
         lsum[hl] *= alpha;
@@ -520,7 +553,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
             wait_vmcnt<LPT>();
           else
             wait_vmcnt<0>();
-          __syncthreads();
+          if constexpr (!KSPLIT) __syncthreads();
           if (t + DV < ntiles)
             issue_v(t + DV, std::integral_constant<int, (S + DV) % VR>{});
           if (t + DK < ntiles)
@@ -534,6 +567,56 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
         }
       });
     }
+  }
+
+  if constexpr (KSPLIT) {
+    // ---- each wave holds (m, l, o) of all 16 heads over its own keys (row
+    // r: heads 4 r ..; the row's 16 lanes split l over keys and o over
+    // dims).  Once every wave is done with the ring, they meet in LDS and
+    // are merged with the log-sum-exp rule: with M the largest of the four
+    // maxima, l = sum 2^(m_w - M) l_w, o = sum 2^(m_w - M) o_w.
+#pragma unroll
+    for (int hl = 0; hl < HW; ++hl) lsum[hl] = row_sum(lsum[hl]);
+    float* const cm = reinterpret_cast<float*>(smem);   // [4 waves][16]
+    float* const cl = cm + WAVES * HPW;                  // [4][16]
+    float* const co = cl + WAVES * HPW;                  // [4][16][128]
+    __syncthreads();
+#pragma unroll
+    for (int hl = 0; hl < HW; ++hl) {
+      const int h = hrow + hl;
+      if (jl == 0) {
+        cm[w * HPW + h] = m[hl];
+        cl[w * HPW + h] = lsum[hl];
+      }
+      float* dst = co + (w * HPW + h) * kD + jl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[16 * e] = o[hl][e];
+    }
+    __syncthreads();
+    // thread: head tid / 16, dims 8 (tid % 16) .. + 7
+    const int h = tid >> 4, d0 = (tid & 15) * 8;
+    float M = cm[h];
+#pragma unroll
+    for (int v = 1; v < WAVES; ++v) M = fmaxf(M, cm[v * HPW + h]);
+    float L = 0.0f, O[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[e] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) {
+      const float c = fast_exp2(cm[v * HPW + h] - M);
+      L += c * cl[v * HPW + h];
+      const float* src = co + (v * HPW + h) * kD + d0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[e] += c * src[e];
+    }
+    float* dst = part + 2 * HPW + h * kD + d0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = O[e];
+    if ((tid & 15) == 0) {
+      part[h] = M;
+      part[HPW + h] = L;
+    }
+    return;
   }
 
   // ---- reduce over the four key groups and the 64 key lanes, write
@@ -672,7 +755,7 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
   } else {
     hipLaunchKernelGGL(
         (decode_split_kernel<kGlobalWaves, kGroup, kGlobalKRing,
-                             kGlobalVRing, false>),
+                             kGlobalVRing, false, true>),
         dim3(p.units), dim3(64 * kGlobalWaves), 0, s, p);
   }
   hipError_t e = hipGetLastError();

@@ -36,12 +36,13 @@ hipError_t launch_kv_append(const AppendParams& p, int B, int count,
 
 // ---------------------------------------------------------------- decode
 constexpr int kDecTile = 64;               // keys per tile
-// Global-layer decode: waves per workgroup (16 / waves query heads each),
-// K and V tile slots in its LDS ring (16 KB each; K tiles are loaded one
-// tile further ahead than V tiles), and how many such workgroups fit one CU
-// (80 KB of LDS each).  Four waves, two workgroups per CU measured fastest:
-// eight waves (two heads each), or three or four workgroups per CU with one
-// slot each, lose more VALU efficiency than they gain.
+// Global-layer decode: waves per workgroup (each takes 16 keys of every
+// tile for all 16 query heads), K and V tile slots in its LDS ring (16 KB
+// each; K tiles are loaded one tile further ahead than V tiles), and how
+// many such workgroups fit one CU (80 KB of LDS each).  Four waves, two
+// workgroups per CU measured fastest: eight waves (two heads each), or three
+// or four workgroups per CU with one slot each, lose more VALU efficiency
+// than they gain.
 constexpr int kGlobalWaves = 4;
 constexpr int kGlobalKRing = 3;
 constexpr int kGlobalVRing = 2;
