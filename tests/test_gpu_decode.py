@@ -53,6 +53,18 @@ def test_decode_ragged_batch_and_edges(kind):
     check_close(got, want, "decode ragged kind=%d" % kind)
 
 
+def test_decode_global_wave_key_groups():
+    """Global layers split each 64-key tile over four waves of 16 keys and
+    merge the waves' sums at the end of the split: contexts of 1 .. 18 keys
+    (only the first wave sees keys), tiles ending on and next to the 16-key
+    group edges, and longer sequences whose last tile is partial, in one
+    ragged batch."""
+    positions = list(range(18)) + [31, 32, 47, 48, 63, 64 * 40 + 5,
+                                    20000 + 17]
+    got, want, _, _ = _decode_case(ga.GLOBAL, positions, seed=1012)
+    check_close(got, want, "decode global wave groups")
+
+
 @pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
 def test_decode_full_context_131072(kind):
     got, want, _, _ = _decode_case(
@@ -110,7 +122,9 @@ def test_decode_constant_v(kind):
 @pytest.mark.parametrize("kind,p,needle", [
     (ga.GLOBAL, 131071, 0), (ga.GLOBAL, 131071, 131071),
     (ga.GLOBAL, 131071, 64 * 37), (ga.GLOBAL, 131071, 64 * 37 - 1),
-    (ga.GLOBAL, 50000, 49999), (ga.LOCAL, 131071, 131071 - 2047),
+    (ga.GLOBAL, 50000, 49999), (ga.GLOBAL, 40, 15), (ga.GLOBAL, 40, 16),
+    (ga.GLOBAL, 3000, 64 * 20 + 47), (ga.GLOBAL, 3000, 64 * 20 + 48),
+    (ga.LOCAL, 131071, 131071 - 2047),
     (ga.LOCAL, 131071, 131071), (ga.LOCAL, 10000, 10000 - 2047 + 64),
     (ga.LOCAL, 4095, 2048), (ga.LOCAL, 4095, 2047 + 2048)])
 def test_decode_needle(kind, p, needle):
