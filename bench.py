@@ -143,11 +143,11 @@ def bench_decode_b1(ga, torch, steps, warmup):
                 for l in pair:
                     ga.attn_decode_append(layers[l], qs[l], step.knews[l],
                                           step.vnews[l], positions, outs[l], ws)
-            ms, _ = time_graph(torch, fn, steps, warmup)
+            ms, _, _ = time_graph(torch, fn, steps, warmup)
             nbytes = sum(kv_bytes_step([kinds[l]], positions) for l in pair)
             name, what = "b1_ctx4096_1local_1global", "2 layers"
         else:
-            ms, _ = time_graph(torch, step, steps, warmup)
+            ms, _, _ = time_graph(torch, step, steps, warmup)
             nbytes = kv_bytes_step(kinds, positions)
             name, what = "b1_ctx%d_52layers" % ctx, "52 layers"
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -159,6 +159,9 @@ def bench_decode_b1(ga, torch, steps, warmup):
 
 
 def time_graph(torch, fn, steps, warmup):
+    """Capture fn once in a HIP graph, replay it `warmup` times untimed,
+    then `steps` times with an event between replays.  Returns (median ms
+    per replay, the graph, mean ms per replay)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -171,36 +174,42 @@ def time_graph(torch, fn, steps, warmup):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         g.replay()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, g
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return median(per), g, sum(per) / len(per)
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
 def time_global_decode(ga, torch, layers, qs, outs, ws, positions, kinds,
                        reps):
-    """Average duration of one global-layer decode call (split kernel +
-    merge kernel) at the step's context, rotating over the 13 global layers
-    so the 256 MB last-level cache cannot serve repeats."""
+    """Duration of one global-layer decode call (split kernel + merge
+    kernel) at the step's context, rotating over the 13 global layers so the
+    256 MB last-level cache cannot serve repeats.  HIP events on the stream
+    the calls are launched on, one between consecutive calls.  Returns
+    (mean ms, median ms) per call."""
     glob = [l for l, k in enumerate(kinds) if k == ga.GLOBAL]
     for l in glob:
         ga.attn_decode(layers[l], qs[l], positions, outs[l], ws)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    n = 0
-    for _ in range(reps):
-        for l in glob:
-            ga.attn_decode(layers[l], qs[l], positions, outs[l], ws)
-            n += 1
-    e1.record()
+    calls = [l for _ in range(reps) for l in glob]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+    ev[0].record()
+    for i, l in enumerate(calls):
+        ga.attn_decode(layers[l], qs[l], positions, outs[l], ws)
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(calls))]
+    return sum(per) / len(per), median(per)
 
 
 def pairs_block(kind, pos0, n, window=2048):
@@ -243,7 +252,7 @@ def bench_verify(ga, torch, layers, kinds, B, reps=5, seed=4004):
             q, kb, vb = blk[l]
             ga.attn_verify(layers[l], q, kb, vb, positions, out, ws)
 
-    ms, _ = time_graph(torch, step, reps, 2)
+    ms, _, _ = time_graph(torch, step, reps, 2)
     flops = 0
     kvb = 0
     for kind in kinds:
@@ -286,7 +295,7 @@ def bench_draft(ga, torch, layers, kinds, B, n_drafter=5, reps=5, seed=4404):
             q, kb, vb = blk[i]
             ga.attn_draft_block(layers[l], q, kb, vb, positions, out, ws)
 
-    ms, _ = time_graph(torch, step, reps, 2)
+    ms, _, _ = time_graph(torch, step, reps, 2)
     flops = len(glob) * B * pairs_block_together(pos0, n) * 4 * ga.HQ * ga.D
     kvb = len(glob) * B * CTX * 1024
     return {"ms_per_step": round(ms, 4),
@@ -345,9 +354,13 @@ def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005):
     return res
 
 
-def cpu_baseline(ga, torch, layers, qs, positions, kinds, budget_s=20.0):
+def cpu_baseline(ga, torch, layers, qs, outs, positions, kinds,
+                 budget_s=20.0):
     """The fp64 oracle on this host: one decode step for sequence 0 over as
-    many layers (in step order) as fit the time budget."""
+    many layers (in step order) as fit the time budget.  The oracle's
+    outputs are also compared with that sequence's outputs of the timed step
+    (max abs <= 2e-2, mean abs <= 2e-3); a miss raises, so no figure is
+    printed for a wrong result."""
     import numpy as np
     import oracle
     import synth_inputs as si
@@ -358,6 +371,7 @@ def cpu_baseline(ga, torch, layers, qs, positions, kinds, budget_s=20.0):
         cores = os.cpu_count() or 1
     p = positions[0]
     done_bytes, done_layers = 0, 0
+    worst_max, worst_mean = 0.0, 0.0
     t0 = time.perf_counter()
     elapsed = 0.0
     for l, kind in enumerate(kinds):
@@ -371,10 +385,18 @@ def cpu_baseline(ga, torch, layers, qs, positions, kinds, budget_s=20.0):
             vb = si.bits(layers[l].v[0, idx])
         qb = si.bits(qs[l][0:1])
         ts = time.perf_counter()
-        oracle.attend(qb, [p], kb, vb, lo, hq=32, hkv=2, d=128,
-                      window=ga.WINDOW if kind == ga.LOCAL else 0,
-                      rope=kind == ga.LOCAL, nthreads=cores)
+        want = oracle.attend(qb, [p], kb, vb, lo, hq=32, hkv=2, d=128,
+                             window=ga.WINDOW if kind == ga.LOCAL else 0,
+                             rope=kind == ga.LOCAL, nthreads=cores)
         elapsed += time.perf_counter() - ts
+        err = np.abs(outs[l][0].cpu().double().numpy() - want[0])
+        worst_max = max(worst_max, float(err.max()))
+        worst_mean = max(worst_mean, float(err.mean()))
+        if not (err.max() <= 2e-2 and err.mean() <= 2e-3):
+            raise RuntimeError(
+                "layer %d (kind %d) of the decode step differs from the "
+                "oracle: max abs %.3e, mean abs %.3e" %
+                (l, kind, err.max(), err.mean()))
         done_bytes += (p + 1 - lo) * 1024
         done_layers += 1
         if time.perf_counter() - t0 > budget_s:
@@ -386,8 +408,10 @@ def cpu_baseline(ga, torch, layers, qs, positions, kinds, budget_s=20.0):
         "kind": "oracle",
         "sample": "fp64 oracle, one decode step of sequence 0 at context %d "
                   "over the first %d of 52 layers (%.1f MB of KV), %.2f s of "
-                  "oracle time" % (p + 1, done_layers, done_bytes / 1e6,
-                                   elapsed),
+                  "oracle time; the step's outputs for those layers match it "
+                  "(worst max abs %.2e, mean abs %.2e)" %
+                  (p + 1, done_layers, done_bytes / 1e6, elapsed, worst_max,
+                   worst_mean),
     }
 
 
@@ -442,22 +466,24 @@ def main():
     print("# setup done: %d layers, batch %d, context %d" % (N_LAYERS, B, CTX),
           file=sys.stderr, flush=True)
     if args.global_decode_calls:
-        kms = time_global_decode(ga, torch, layers, qs, outs, ws, positions,
-                                 kinds, args.global_decode_calls)
+        kms, _ = time_global_decode(ga, torch, layers, qs, outs, ws,
+                                    positions, kinds, args.global_decode_calls)
         print(json.dumps({"global_decode_call_ms": round(kms, 5),
                           "batch": B, "keys": pos + 1}), flush=True)
         return
 
-    ms, _graph = time_graph(torch, step, args.steps, args.warmup)
+    ms, _graph, ms_mean = time_graph(torch, step, args.steps, args.warmup)
     check_step_outputs(ga, torch, layers, qs, outs, positions, kinds)
     kvb = kv_bytes_step(kinds, positions)
     value = kvb / (ms * 1e-3) / 1e9
 
-    ms_local, _ = time_graph(torch, step.local_only, args.steps, args.warmup)
-    ms_global, _ = time_graph(torch, step.global_only, args.steps, args.warmup)
+    ms_local, _, _ = time_graph(torch, step.local_only, args.steps,
+                                args.warmup)
+    ms_global, _, _ = time_graph(torch, step.global_only, args.steps,
+                                 args.warmup)
 
-    kms = time_global_decode(ga, torch, layers, qs, outs, ws, positions,
-                             kinds, args.kernel_reps)
+    kms, kms_med = time_global_decode(ga, torch, layers, qs, outs, ws,
+                                      positions, kinds, args.kernel_reps)
     kbytes = B * (pos + 1) * 1024
     achieved = kbytes / (kms * 1e-3) / 1e9
 
@@ -469,6 +495,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_mean": round(ms_mean, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -493,12 +520,13 @@ def main():
             "traffic": measured_traffic(B),
             "traffic_unit": "bytes per launch (HBM fetched + written)",
             "avg_ms": round(kms, 5),
+            "median_ms": round(kms_med, 5),
             "algorithmic_bytes": kbytes,
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(ga, torch, layers, qs, positions,
-                                            kinds)
+        line["cpu_baseline"] = cpu_baseline(ga, torch, layers, qs, outs,
+                                            positions, kinds)
     if not args.no_extras:
         line["verify"] = bench_verify(ga, torch, layers, kinds, 1)
         print("# verify done", file=sys.stderr, flush=True)

@@ -22,7 +22,7 @@ __all__ = [
     "MAX_VERIFY", "attn_verify", "attn_draft_block", "attn_prefill", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
     "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
     "attn_decode", "attn_decode_append", "attn_decode_dev", "workspace_bytes", "workspace", "status_string", "abi_version",
-    "library_path", "layer_kind",
+    "library_path", "layer_kind", "NUM_LAYERS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -32,6 +32,7 @@ LOCAL, GLOBAL = 0, 1
 OP_DECODE, OP_VERIFY, OP_PREFILL, OP_DRAFT = 0, 1, 2, 3
 MAX_VERIFY = 16
 HQ, HKV, D, WINDOW, MAX_CONTEXT, MAX_BATCH = 32, 2, 128, 2048, 131072, 64
+NUM_LAYERS = 52
 ROPE_THETA = 10000.0
 
 _lib = None
@@ -70,6 +71,8 @@ def _load():
         p, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         L = ctypes.POINTER(_CLayer)
         lib.gqa_abi_version.restype = i32
+        lib.gqa_layer_kind.restype = i32
+        lib.gqa_layer_kind.argtypes = [i32]
         lib.gqa_status_string.restype = ctypes.c_char_p
         lib.gqa_status_string.argtypes = [i32]
         lib.gqa_workspace_bytes.restype = ctypes.c_size_t
@@ -110,8 +113,13 @@ def workspace_bytes(op: int, kind: int, B: int, n: int, max_ctx: int) -> int:
 
 
 def layer_kind(layer_index: int) -> int:
-    """Three local layers then one global layer, repeating."""
-    return GLOBAL if layer_index % 4 == 3 else LOCAL
+    """Kind of layer ``layer_index`` (0 .. NUM_LAYERS-1) of the stack, as the
+    library's schedule gives it (``gqa_layer_kind``: three local layers, then
+    one global layer, repeating)."""
+    kind = _load().gqa_layer_kind(int(layer_index))
+    if kind < 0:
+        raise GqaError(kind, "gqa_layer_kind")
+    return kind
 
 
 class Layer:

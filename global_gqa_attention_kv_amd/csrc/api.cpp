@@ -4,93 +4,36 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "internal.h"
 #include "validate.h"
 
 namespace gqa {
 
-namespace {
-// Global-layer decode: as many split-kernel workgroups as fit the 256 CUs at
-// once, so the launch runs as one full round (a partial second round would
-// leave part of the device idle at the end).
-constexpr int kDecodeTargetWGs = 256 * kGlobalWGsPerCU;
-static_assert(kDecodeTargetWGs / 2 <= kMaxSplits, "merge kernel capacity");
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-}  // namespace
-
-DecodePlan plan_decode(int kind, int B, int64_t max_keys) {
-  const int64_t tiles = (max_keys + kDecTile - 1) / kDecTile;
-  DecodePlan p;
-  p.heads_per_wg = kGroup;
-  if (kind == GQA_LOCAL) {
-    if (B <= kLocalSmallMaxBatch) p.heads_per_wg = kLocalSmallHeads;
-    // the window is 32 tiles: one tile per workgroup up to batch 4 (256
-    // workgroups), then longer splits so a launch stays near 256
-    p.tiles_per_split = B >= 8 ? B / 4 : 1;
-    if (p.tiles_per_split > (int)tiles) p.tiles_per_split = (int)tiles;
-    if (p.tiles_per_split < 1) p.tiles_per_split = 1;
-    p.splits = (int)((tiles + p.tiles_per_split - 1) / p.tiles_per_split);
-    if (p.splits < 1) p.splits = 1;
-    return p;
-  }
-  int64_t want = kDecodeTargetWGs / (2 * B);
-  if (want < 1) want = 1;
-  int64_t per = (tiles + want - 1) / want;
-  if (per < 1) per = 1;
-  p.tiles_per_split = (int)per;
-  p.splits = (int)((tiles + per - 1) / per);
-  if (p.splits < 1) p.splits = 1;
-  return p;
-}
-
-// Workspace: the partial sums [B][2][head groups][splits][heads x 130]
-// floats (m[heads], l[heads], o[heads][128] per split).
-size_t decode_ws_bytes(int B, const DecodePlan& plan) {
-  return align256((size_t)B * kHkv * plan.splits * kGroup * (kD + 2) *
-                  sizeof(float));
-}
-
-// Block operations.  Workgroups take 16 query tokens of one KV head; the
-// key range is split across workgroups (down to one 64-key tile each) only
-// when the query groups alone cannot fill the device with kBlockTargetWGs
-// workgroups: always for verification (<= 16 tokens), for short prefills.
-namespace {
-constexpr int kBlockTargetWGs = 256;
-}
-
-BlockPlan plan_block(int kind, int B, int n, int64_t max_keys) {
-  BlockPlan p;
-  p.qpw = kBlkQpw;
-  p.qgroups = (n + p.qpw - 1) / p.qpw;
-  // keys one workgroup may see: its window (local) or everything before it
-  const int64_t wg_keys =
-      kind == GQA_LOCAL ? (int64_t)kW - 1 + p.qpw : max_keys;
-  const int64_t tiles = (wg_keys + kBlkTile - 1) / kBlkTile;
-  const int64_t groups = (int64_t)p.qgroups * kHkv * B;
-  int64_t splits = 1;
-  if (groups < kBlockTargetWGs)
-    splits = (kBlockTargetWGs + groups - 1) / groups;
-  // down to one tile per workgroup (measured on the local verify: one tile
-  // per workgroup beat two now that split partials are bf16 rows)
-  if (splits > tiles) splits = tiles;
-  if (splits < 1) splits = 1;
-  p.splits = (int)splits;
-  // local layers without key splits read pre-rotated keys from the
-  // workspace; split calls rotate each tile in LDS
-  p.klin_bytes = kind == GQA_LOCAL && p.splits == 1
-                     ? align256((size_t)B * ((size_t)kW + n) * kTokenElems * 2)
-                     : 0;
-  p.part_bytes = p.splits > 1
-                     ? align256((size_t)B * kHkv * p.qgroups * p.splits *
-                                p.qpw * kGroup * 68 * sizeof(float))
-                     : 0;
-  return p;
-}
-
-// Rotated keys (local layers), then partial sums (split keys).
-size_t block_ws_bytes(const BlockPlan& plan) {
-  const size_t n = plan.klin_bytes + plan.part_bytes;
-  return n ? n : 256;
+// Compute units and XCDs of the device current on the calling thread, read
+// from the runtime once per device and remembered (the planners size the
+// launches for them).  Without a device (host-only use) the shape of a full
+// MI355X is assumed.
+DeviceShape current_device_shape() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // cus << 8 | xcds, 0 = unread
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return kDefaultShape;
+  const int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return DeviceShape{c >> 8, c & 255};
+  int cus = 0, xcds = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess ||
+      cus <= 0 || cus >= (1 << 22))
+    return kDefaultShape;
+  if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) !=
+          hipSuccess ||
+      xcds <= 0 || xcds > 255)
+    xcds = 1;
+  cache[dev].store(cus << 8 | xcds, std::memory_order_relaxed);
+  return DeviceShape{cus, xcds};
 }
 
 }  // namespace gqa
@@ -100,6 +43,11 @@ using namespace gqa;
 extern "C" {
 
 int gqa_abi_version(void) { return GQA_ABI_VERSION; }
+
+int gqa_layer_kind(int layer) {
+  if (layer < 0 || layer >= GQA_NUM_LAYERS) return GQA_ERR_INVALID_ARG;
+  return layer % 4 == 3 ? GQA_GLOBAL : GQA_LOCAL;
+}
 
 const char* gqa_status_string(int status) {
   switch (status) {
@@ -121,7 +69,8 @@ size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx) {
   switch (op) {
     case GQA_OP_DECODE: {
       const int64_t keys = visible_keys(kind, max_ctx - 1);
-      return decode_ws_bytes(B, plan_decode(kind, B, keys));
+      return decode_ws_bytes(
+          B, plan_decode(kind, B, keys, current_device_shape()));
     }
     case GQA_OP_DRAFT:
       if (kind != GQA_GLOBAL) return 0;
@@ -131,7 +80,8 @@ size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx) {
       const bool verify = op != GQA_OP_PREFILL;
       if (n > (verify ? GQA_MAX_VERIFY : GQA_MAX_CONTEXT)) return 0;
       const int64_t keys = visible_keys(kind, max_ctx - 1);
-      return block_ws_bytes(plan_block(kind, B, n, keys));
+      return block_ws_bytes(
+          plan_block(kind, B, n, keys, current_device_shape()));
     }
     default:
       return 0;
@@ -184,7 +134,8 @@ static int decode_impl(const gqa_layer* layer, const void* q,
     if (((uintptr_t)k_new & 15u) || ((uintptr_t)v_new & 15u))
       return GQA_ERR_MISALIGNED;
   }
-  const DecodePlan plan = plan_decode(layer->kind, B, max_keys);
+  const DeviceShape dev = current_device_shape();
+  const DecodePlan plan = plan_decode(layer->kind, B, max_keys, dev);
   if (plan.splits > kMaxSplits) return GQA_ERR_UNSUPPORTED;
   const size_t need = decode_ws_bytes(B, plan);
   if (!ws) return GQA_ERR_INVALID_ARG;
@@ -206,6 +157,7 @@ static int decode_impl(const gqa_layer* layer, const void* q,
   p.splits = plan.splits;
   p.tiles_per_split = plan.tiles_per_split;
   p.units = B * kHkv * plan.splits;
+  p.xcds = dev.xcds;
   const bool local = layer->kind == GQA_LOCAL;
   if (local) {
     // revolutions per position of frequency c: theta^(-c/64) / (2 pi),
@@ -256,7 +208,8 @@ static int block_impl(const gqa_layer* layer, const void* q,
                        &max_keys);
   if (rc != GQA_OK) return rc;
   if (together && layer->kind != GQA_GLOBAL) return GQA_ERR_UNSUPPORTED;
-  const BlockPlan plan = plan_block(layer->kind, B, n, max_keys);
+  const BlockPlan plan =
+      plan_block(layer->kind, B, n, max_keys, current_device_shape());
   if (!ws) return GQA_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
   if (ws_bytes < block_ws_bytes(plan)) return GQA_ERR_WS_TOO_SMALL;

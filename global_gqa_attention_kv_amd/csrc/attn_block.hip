@@ -741,11 +741,11 @@ __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
 }
 
 template <bool LOCAL, bool OUT_F32>
-hipError_t launch_main(const BlockParams& p, int B, hipStream_t s) {
-  const int items = p.splits * p.qgroups * kHkv * B;
-  // without key splits: at most one workgroup per CU, each walking its items
-  const int walks = p.splits > 1 ? 1 : (items + kCUs - 1) / kCUs;
-  const dim3 grid((items + walks - 1) / walks);
+hipError_t launch_main(const BlockParams& p, const BlockPlan& plan, int B,
+                       hipStream_t s) {
+  // without key splits: at most one workgroup per CU, each walking its
+  // items (the kernel derives the walk from the grid)
+  const dim3 grid(plan.grid);
   const dim3 block(kWaves * 64);
   if (p.splits > 1) {
     hipLaunchKernelGGL((block_attn_kernel<LOCAL, true, OUT_F32>), grid, block,
@@ -765,7 +765,9 @@ hipError_t launch_main(const BlockParams& p, int B, hipStream_t s) {
 
 hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
                         bool local, bool out_f32, int B, hipStream_t s) {
-  if (plan.qpw != kBlkQpw || p.splits > kMaxSplits) return hipErrorInvalidValue;
+  if (plan.qpw != kBlkQpw || p.splits > kMaxSplits || plan.grid < 1 ||
+      (p.splits > 1 && plan.grid != p.splits * p.qgroups * kHkv * B))
+    return hipErrorInvalidValue;
   if (local) {
     if (p.splits == 1) {  // keys rotated once into the workspace
       hipLaunchKernelGGL(rope_keys_kernel, dim3((unsigned)p.klin_rows, B),
@@ -773,11 +775,11 @@ hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    return out_f32 ? launch_main<true, true>(p, B, s)
-                   : launch_main<true, false>(p, B, s);
+    return out_f32 ? launch_main<true, true>(p, plan, B, s)
+                   : launch_main<true, false>(p, plan, B, s);
   }
-  return out_f32 ? launch_main<false, true>(p, B, s)
-                 : launch_main<false, false>(p, B, s);
+  return out_f32 ? launch_main<false, true>(p, plan, B, s)
+                 : launch_main<false, false>(p, plan, B, s);
 }
 
 }  // namespace gqa

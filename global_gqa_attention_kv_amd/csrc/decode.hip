@@ -157,14 +157,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // workgroup -> (unit, head group).  Consecutive workgroup ids go to
-  // different XCDs round-robin, so the HG workgroups of one unit are placed
-  // 8 ids apart: same XCD, same L2, dispatched together.
+  // workgroup -> (unit, head group).  Consecutive workgroup ids go to the
+  // device's XCDs round-robin, so the HG workgroups of one unit are placed
+  // X = p.xcds ids apart: same XCD, same L2, dispatched together.  (The map
+  // is one-to-one for any X; only the L2 sharing depends on it.)
   int unit = blockIdx.x, hg = 0;
   if constexpr (HG > 1) {
-    const int r = blockIdx.x % (8 * HG);
-    unit = (blockIdx.x / (8 * HG)) * 8 + (r & 7);
-    hg = r >> 3;
+    const int X = p.xcds;
+    const int r = blockIdx.x % (X * HG);
+    unit = (blockIdx.x / (X * HG)) * X + r % X;
+    hg = r / X;
   }
   if (unit >= p.units) return;  // padding of the XCD-aware grid
   const int split = unit % p.splits;
@@ -744,7 +746,7 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
   if (local && plan.heads_per_wg == kLocalSmallHeads) {
     // small batches: 4 workgroups (head groups) share each tile
     constexpr int HG = kGroup / kLocalSmallHeads;
-    const int grid = (p.units + 7) / 8 * 8 * HG;
+    const int grid = (p.units + p.xcds - 1) / p.xcds * p.xcds * HG;
     if (p.tiles_per_split != 1) return hipErrorInvalidValue;
     hipLaunchKernelGGL(
         (decode_split_kernel<kLocalSmallWaves, kLocalSmallHeads, 1, 1, true>),

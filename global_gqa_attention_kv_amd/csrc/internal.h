@@ -6,16 +6,9 @@
 #include <stdint.h>
 
 #include "gqa_attn.h"
+#include "plan.h"
 
 namespace gqa {
-
-constexpr int kHq = GQA_NUM_Q_HEADS;      // 32 query heads
-constexpr int kHkv = GQA_NUM_KV_HEADS;    // 2 KV heads
-constexpr int kGroup = kHq / kHkv;        // 16 query heads per KV head
-constexpr int kD = GQA_HEAD_DIM;          // 128
-constexpr int kW = GQA_WINDOW;            // 2048-slot ring
-constexpr int kMaxBatch = GQA_MAX_BATCH;
-constexpr int kTokenElems = kHkv * kD;    // 256 bf16 per token per cache
 
 // ---------------------------------------------------------------- append
 struct AppendParams {
@@ -35,39 +28,23 @@ hipError_t launch_kv_append(const AppendParams& p, int B, int count,
                             hipStream_t s);
 
 // ---------------------------------------------------------------- decode
-constexpr int kDecTile = 64;               // keys per tile
 // Global-layer decode: waves per workgroup (each takes 16 keys of every
-// tile for all 16 query heads), K and V tile slots in its LDS ring (16 KB
-// each; K tiles are loaded one tile further ahead than V tiles), and how
-// many such workgroups fit one CU (80 KB of LDS each).  Four waves, two
-// workgroups per CU measured fastest: eight waves (two heads each), or three
-// or four workgroups per CU with one slot each, lose more VALU efficiency
-// than they gain.
+// tile for all 16 query heads) and K and V tile slots in its LDS ring (16 KB
+// each; K tiles are loaded one tile further ahead than V tiles); two such
+// workgroups fit one CU (kGlobalWGsPerCU, 80 KB of LDS each).  Four waves,
+// two workgroups per CU measured fastest: eight waves (two heads each), or
+// three or four workgroups per CU with one slot each, lose more VALU
+// efficiency than they gain.
 constexpr int kGlobalWaves = 4;
 constexpr int kGlobalKRing = 3;
 constexpr int kGlobalVRing = 2;
-constexpr int kGlobalWGsPerCU = 2;
 // Local-layer decode (latency-bound, one tile per workgroup): 8 waves of 2
 // heads put more waves behind each tile than 4 waves of 4 heads.
 constexpr int kLocalWaves = 8;
-// Local layers at small batch: the 16 heads of a KV head split over 4
-// workgroups of 2 waves (2 heads each), which read the same tile (L2 hits
-// after the first) and each do a quarter of the products.
-constexpr int kLocalSmallHeads = 4;
+// Local layers at small batch: the 16 heads of a KV head split over
+// workgroups of kLocalSmallHeads heads in 2 waves, which read the same tile
+// (L2 hits after the first) and each do a quarter of the products.
 constexpr int kLocalSmallWaves = 2;
-constexpr int kLocalSmallMaxBatch = 2;
-// Most key splits of one decode call (the merge kernel loads them all at once).
-constexpr int kMaxSplits = 256;
-
-// A workgroup serves all 16 query heads of one (sequence, KV head) over a
-// split of tiles_per_split tiles; a second kernel merges the splits.
-struct DecodePlan {
-  int splits;           // S: key splits per (sequence, KV head)
-  int tiles_per_split;  // tiles of kDecTile keys per split
-  int heads_per_wg;     // 16, or kLocalSmallHeads (head groups share a tile)
-};
-DecodePlan plan_decode(int kind, int B, int64_t max_keys);
-size_t decode_ws_bytes(int B, const DecodePlan& plan);
 
 struct DecodeParams {
   const uint16_t* k;       // cache base (sequence 0, slot 0, head 0)
@@ -84,6 +61,7 @@ struct DecodeParams {
   int32_t splits;
   int32_t tiles_per_split;
   int32_t units;           // B * 2 * splits
+  int32_t xcds;            // XCDs of the device (workgroup placement)
   float rope_rev[kD / 2];  // local: theta^(-c/64) / (2 pi), revolutions per position
   const int64_t* pos_dev;  // device positions [B] (read instead of pos), or null
   int64_t max_pos;         // with pos_dev: positions above it are not attended
@@ -99,20 +77,7 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
 // output, keys split across workgroups) and a drafted block whose tokens
 // are predicted together (as verification, without the causal order inside
 // the block).
-constexpr int kBlkTile = 64;               // keys per tile
-constexpr int kCUs = 256;                  // compute units of an MI355X
-constexpr int kBlkQpw = 16;                // query tokens per workgroup
 constexpr int kMaxPrefill = GQA_MAX_CONTEXT;
-
-struct BlockPlan {
-  int qpw;          // query tokens per workgroup (x 16 heads = rows)
-  int qgroups;      // ceil(n / qpw)
-  int splits;       // key splits (1 = no partials)
-  size_t klin_bytes;   // local: pre-rotated keys
-  size_t part_bytes;   // split partials
-};
-BlockPlan plan_block(int kind, int B, int n, int64_t max_keys);
-size_t block_ws_bytes(const BlockPlan& plan);
 
 struct BlockParams {
   const uint16_t* q;        // [B][n][32][128]

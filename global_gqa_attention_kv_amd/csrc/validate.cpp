@@ -10,7 +10,9 @@
 namespace gqa {
 
 namespace {
-constexpr int64_t kMaxPos = INT32_MAX;  // positions fit 32-bit kernel math
+// Positions stay below 2^31 - 4096, so the kernels' 32-bit key-range
+// arithmetic (a block's last key + 1, a tile's first key + 64) cannot wrap.
+constexpr int64_t kMaxPos = GQA_MAX_POSITION;
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 }  // namespace
 

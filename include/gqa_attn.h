@@ -56,6 +56,11 @@ extern "C" {
 #define GQA_MAX_CONTEXT 131072
 #define GQA_MAX_BATCH 64
 #define GQA_MAX_VERIFY 16
+#define GQA_NUM_LAYERS 52
+/* Largest position any token may have (local layers; global layers are
+ * bounded by their capacity): 2^31 - 4097, so the kernels' 32-bit key-range
+ * arithmetic never wraps. */
+#define GQA_MAX_POSITION 2147479551
 
 /* Layer kinds. */
 #define GQA_LOCAL 0
@@ -70,7 +75,8 @@ extern "C" {
 /* Status codes. */
 #define GQA_OK 0
 #define GQA_ERR_INVALID_ARG (-1)  /* null pointer, B or n out of range      */
-#define GQA_ERR_POS_RANGE (-2)    /* position < 0, or past a global cache   */
+#define GQA_ERR_POS_RANGE (-2)    /* position < 0, past a global cache, or
+                                     above GQA_MAX_POSITION                 */
 #define GQA_ERR_MISALIGNED (-3)   /* a pointer or stride not 16-B aligned    */
 #define GQA_ERR_WS_TOO_SMALL (-4) /* workspace smaller than required        */
 #define GQA_ERR_UNSUPPORTED (-5)  /* layer descriptor outside compiled shape */
@@ -94,6 +100,19 @@ typedef struct gqa_layer {
   void* v;
   int64_t seq_stride;
 } gqa_layer;
+
+/* Kind of layer `layer` (0-based) of the 52-layer stack: GQA_GLOBAL when
+ * layer % 4 == 3, GQA_LOCAL otherwise -- three local layers, then one
+ * global layer, 13 times (39 local + 13 global).  Returns
+ * GQA_ERR_INVALID_ARG for an index outside 0 .. GQA_NUM_LAYERS-1.  The
+ * caller describes layer l's cache with this kind (local: window
+ * GQA_WINDOW, capacity GQA_WINDOW, RoPE; global: window 0, linear cache,
+ * no RoPE).
+ * Pages: shishifenxi.com section 01 (52 layers, a repeating cycle of three
+ * sliding-window layers followed by one full-attention layer);
+ * runtimewire.com "Narrow cache" (every fourth layer is global: 39
+ * sliding-window layers and 13 full layers). */
+int gqa_layer_kind(int layer);
 
 /* Append n tokens per sequence to a layer's cache (bit-exact copy).
  * k_new, v_new: [B][n][2][128] bf16; token t of sequence b has position

@@ -235,3 +235,40 @@ def test_block_validation(lib, fn):
     # local layers need room for the rotated window in the workspace
     loc = ga.workspace_bytes(ga.OP_PREFILL, ga.LOCAL, 1, 4096, 131072)
     assert loc >= (2048 + 4096) * 512
+
+
+def test_layer_kind_schedule(lib):
+    """The library's layer schedule equals the oracle's reading of the pages
+    (three local layers then one global: 39 + 13 of 52) and refuses indices
+    outside the stack."""
+    import oracle
+    D = _defines()
+    n = D["GQA_NUM_LAYERS"]
+    assert n == 52 == ga.NUM_LAYERS
+    kinds = [lib.gqa_layer_kind(l) for l in range(n)]
+    assert kinds == [oracle.layer_kind(l) for l in range(n)]
+    assert kinds == [ga.layer_kind(l) for l in range(n)]
+    assert kinds.count(ga.LOCAL) == 39 and kinds.count(ga.GLOBAL) == 13
+    assert kinds[:4] == [ga.LOCAL, ga.LOCAL, ga.LOCAL, ga.GLOBAL]
+    for bad in (-1, n, 1 << 20):
+        assert lib.gqa_layer_kind(bad) == E_ARG
+    with pytest.raises(ga.GqaError):
+        ga.layer_kind(n)
+
+
+def test_position_bound(lib):
+    """Positions above GQA_MAX_POSITION are refused before any launch (the
+    kernels' 32-bit key-range arithmetic would wrap near 2^31); positions at
+    the bound pass validation and stop at the (empty) workspace check."""
+    top = _defines()["GQA_MAX_POSITION"]
+    assert top == 2 ** 31 - 4097
+    L = _layer(kind=ga.LOCAL)
+    for fn in ("gqa_attn_verify", "gqa_attn_prefill"):
+        f = getattr(lib, fn)
+        assert f(ctypes.byref(L), FAKE, FAKE, FAKE, _pos(top - 14), 1, 16,
+                 FAKE, FAKE, 1 << 30, None) == E_POS
+        assert f(ctypes.byref(L), FAKE, FAKE, FAKE, _pos(top - 15), 1, 16,
+                 FAKE, FAKE, 0, None) == E_WS
+    assert _decode(lib, L, pos=_pos(top + 1)) == E_POS
+    assert _decode(lib, L, pos=_pos(top), ws_bytes=0) == E_WS
+    assert _append(lib, L, n=2, pos=_pos(top)) == E_POS

@@ -70,7 +70,8 @@ def test_decode_full_context_131072(kind):
     got, want, _, _ = _decode_case(
         kind, [131071], seed=1003,
         capacity=ga.MAX_CONTEXT if kind == ga.GLOBAL else None)
-    check_close(got, want, "decode ctx131072 kind=%d" % kind)
+    check_close(got, want, "decode ctx131072 kind=%d" % kind,
+                ctx=131072 if kind == ga.GLOBAL else ga.WINDOW)
 
 
 @pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
@@ -87,7 +88,7 @@ def test_decode_batch4_131072_global():
     positions = [131071, 131071, 100000, 77777]
     got, want, _, _ = _decode_case(ga.GLOBAL, positions, seed=1004,
                                    capacity=ga.MAX_CONTEXT)
-    check_close(got, want, "decode B=4 ctx131072 global")
+    check_close(got, want, "decode B=4 ctx131072 global", ctx=131072)
 
 
 @pytest.mark.parametrize("kind,p", [(ga.LOCAL, 5000), (ga.LOCAL, 1000),
@@ -134,7 +135,8 @@ def test_decode_needle(kind, p, needle):
     capacity = ga.MAX_CONTEXT if kind == ga.GLOBAL else None
     got, want, _, _ = _decode_case(kind, [p], seed=1007, q_cpu=q,
                                    streams=[(k, v)], capacity=capacity)
-    check_close(got, want, "needle kind=%d p=%d at %d" % (kind, p, needle))
+    check_close(got, want, "needle kind=%d p=%d at %d" % (kind, p, needle),
+                ctx=p + 1 if kind == ga.GLOBAL else ga.WINDOW)
     vn = v[needle].double().numpy()
     target = np.repeat(vn, 16, axis=0)
     if kind == ga.LOCAL:

@@ -52,7 +52,7 @@ def test_draft_full_size_131056():
     out = ga.attn_draft_block(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
     torch.cuda.synchronize()
     want = _oracle_together(q, streams, pos0, n)
-    check_close(out.cpu().numpy(), want, "draft 131056+16")
+    check_close(out.cpu().numpy(), want, "draft 131056+16", ctx=131072)
 
 
 @pytest.mark.parametrize("needle", [0, 64 * 37 - 1, 64 * 37, 131055,
@@ -76,7 +76,7 @@ def test_draft_needle(needle):
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     want = _oracle_together(q, [(k, v)], pos0, n)
-    check_close(got, want, "draft needle at %d" % needle)
+    check_close(got, want, "draft needle at %d" % needle, ctx=131072)
     target = np.repeat(v[needle].double().numpy(), 16, axis=0)
     for r in range(n):
         assert np.abs(got[0, r] - target).max() < 0.05, r
