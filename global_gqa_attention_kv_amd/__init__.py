@@ -21,7 +21,8 @@ __all__ = [
     "LOCAL", "GLOBAL", "OP_DECODE", "OP_VERIFY", "OP_PREFILL", "OP_DRAFT",
     "MAX_VERIFY", "attn_verify", "attn_draft_block", "attn_prefill", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
     "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
-    "attn_decode", "attn_decode_append", "attn_decode_dev", "workspace_bytes", "workspace", "status_string", "abi_version",
+    "attn_decode", "attn_decode_append", "attn_decode_dev",
+    "attn_decode_noalloc", "workspace_bytes", "workspace", "status_string", "abi_version",
     "library_path", "layer_kind", "NUM_LAYERS",
 ]
 
@@ -96,6 +97,8 @@ def _load():
         lib.gqa_attn_decode_dev.restype = i32
         lib.gqa_attn_decode_dev.argtypes = [L, p, p, p, p, i64, i32, p, p,
                                             ctypes.c_size_t, p]
+        lib.gqa_attn_decode_noalloc.restype = i32
+        lib.gqa_attn_decode_noalloc.argtypes = [L, p, p, p, p, i32, p, p]
         _lib = lib
     return _lib
 
@@ -286,6 +289,34 @@ def attn_decode_dev(layer: Layer, q, pos_dev, max_pos, out=None, ws=None,
                                      _stream(stream))
     if rc != 0:
         raise GqaError(rc, "gqa_attn_decode_dev")
+    return out
+
+
+def attn_decode_noalloc(layer: Layer, q, pos, out=None, k_new=None,
+                        v_new=None, stream=None):
+    """Decode without a workspace (the library's device-resident scratch
+    holds the split partials), for callers that cannot allocate, e.g. under
+    graph capture.  k_new / v_new: both None (attend only) or bf16
+    [B, 1, 2, 128] (append at pos, then attend).  Pass ``out`` to allocate
+    nothing here either.  Calls overlapping in time on one GPU race; make the
+    first call on a device outside a graph capture.
+    Returns out: fp32 [B, 32, 128]."""
+    B = int(q.shape[0])
+    qp = _dev(q, torch.bfloat16, (B, HQ, D), "q")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    kp = vp = None
+    if k_new is not None:
+        kp = _dev(k_new, torch.bfloat16, (B, 1, HKV, D), "k_new")
+        vp = _dev(v_new, torch.bfloat16, (B, 1, HKV, D), "v_new")
+    if out is None:
+        out = torch.empty((B, HQ, D), dtype=torch.float32, device=q.device)
+    op = _dev(out, torch.float32, (B, HQ, D), "out")
+    rc = _load().gqa_attn_decode_noalloc(layer.c_ref, qp, kp, vp,
+                                         _positions(pos, B), B, op,
+                                         _stream(stream))
+    if rc != 0:
+        raise GqaError(rc, "gqa_attn_decode_noalloc")
     return out
 
 

@@ -114,7 +114,7 @@ static int decode_impl(const gqa_layer* layer, const void* q,
                        const int64_t* pos, int B, float* out, void* ws,
                        size_t ws_bytes, void* stream,
                        const int64_t* pos_dev = nullptr,
-                       int64_t max_pos = 0) {
+                       int64_t max_pos = 0, bool noalloc = false) {
   int64_t max_keys = 0;
   int rc;
   if (pos_dev) {
@@ -138,6 +138,13 @@ static int decode_impl(const gqa_layer* layer, const void* q,
   const DecodePlan plan = plan_decode(layer->kind, B, max_keys, dev);
   if (plan.splits > kMaxSplits) return GQA_ERR_UNSUPPORTED;
   const size_t need = decode_ws_bytes(B, plan);
+  if (noalloc) {
+    // the partials go to the device-resident scratch
+    if (need > kNoAllocScratchBytes) return GQA_ERR_WS_TOO_SMALL;
+    ws = noalloc_scratch();
+    ws_bytes = kNoAllocScratchBytes;
+    if (!ws) return GQA_ERR_HIP;
+  }
   if (!ws) return GQA_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
   if (ws_bytes < need) return GQA_ERR_WS_TOO_SMALL;
@@ -196,6 +203,14 @@ int gqa_attn_decode_dev(const gqa_layer* layer, const void* q,
   if (!pos_dev) return GQA_ERR_INVALID_ARG;
   return decode_impl(layer, q, k_new, v_new, nullptr, B, out, ws, ws_bytes,
                      stream, pos_dev, max_pos);
+}
+
+int gqa_attn_decode_noalloc(const gqa_layer* layer, const void* q,
+                            const void* k_new, const void* v_new,
+                            const int64_t* pos, int B, float* out,
+                            void* stream) {
+  return decode_impl(layer, q, k_new, v_new, pos, B, out, nullptr, 0, stream,
+                     nullptr, 0, true);
 }
 
 static int block_impl(const gqa_layer* layer, const void* q,

@@ -70,6 +70,11 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
                          bool local, int B, hipStream_t s);
 
+// Device address of the current device's copy of the no-allocation scratch
+// (kNoAllocScratchBytes), looked up on the first call on each device; null
+// when there is no device or the lookup fails.
+void* noalloc_scratch();
+
 // ---------------------------------------------------------------- block
 // A block of n query tokens per sequence at positions pos0 .. pos0+n-1 whose
 // K/V (k_blk, v_blk) are not in the cache yet: chunked prefill (n up to a

@@ -39,6 +39,13 @@ constexpr int kLocalSmallMaxBatch = 2;
 // once).
 constexpr int kMaxSplits = 256;
 
+// Device-resident scratch of the entry point that allocates nothing
+// (gqa_attn_decode_noalloc): room for the decode partials of every batch
+// size and context on a 256-CU device (the largest, batch 1 or 2 at 131072
+// keys, needs 4.3 MB).
+constexpr size_t kNoAllocScratchBytes = GQA_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes % 256 == 0, "scratch alignment");
+
 // A decode workgroup serves all 16 query heads (or one head group) of one
 // (sequence, KV head) over a split of tiles_per_split tiles.
 struct DecodePlan {

@@ -21,9 +21,11 @@
  *   - All tensors are device pointers, bf16 unless stated, dense row-major,
  *     16-byte aligned.  Positions are HOST arrays of int64, one per sequence.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
- *     stream).  The library never allocates, frees or synchronises, keeps no
- *     global mutable state and is safe to call from several threads on
- *     different streams.
+ *     stream).  The library never allocates, frees or synchronises.  Its only
+ *     global state is a per-device record of the device's compute-unit and
+ *     XCD counts (read once, used to size launches) and the device-resident
+ *     scratch of gqa_attn_decode_noalloc; every other entry point is safe to
+ *     call from several threads on different streams.
  *   - Arguments are validated on the host before anything is launched; a
  *     non-zero return means nothing was enqueued (except GQA_ERR_HIP, which
  *     reports a failed launch).  Faults inside a kernel surface at the
@@ -61,6 +63,8 @@ extern "C" {
  * bounded by their capacity): 2^31 - 4097, so the kernels' 32-bit key-range
  * arithmetic never wraps. */
 #define GQA_MAX_POSITION 2147479551
+/* Device-resident scratch of gqa_attn_decode_noalloc, per GPU (8 MiB). */
+#define GQA_NOALLOC_SCRATCH_BYTES 8388608
 
 /* Layer kinds. */
 #define GQA_LOCAL 0
@@ -167,6 +171,26 @@ int gqa_attn_decode_dev(const gqa_layer* layer, const void* q,
                         const void* k_new, const void* v_new,
                         const int64_t* pos_dev, int64_t max_pos, int B,
                         float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* gqa_attn_decode / gqa_attn_decode_append without a workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  k_new, v_new: both null
+ * (attend only, as gqa_attn_decode) or both given (append the token, then
+ * attend, as gqa_attn_decode_append); other arguments and layouts as
+ * gqa_attn_decode, same kernels and results.  The split partials go to a
+ * device-resident scratch array of GQA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends; the call
+ * allocates nothing.  A call whose partials need more returns
+ * GQA_ERR_WS_TOO_SMALL (on a 256-CU MI355X none does: every batch size and
+ * context needs at most 4.3 MB).  Every call on one GPU shares that GPU's
+ * scratch: calls that may overlap in time on one GPU (different streams,
+ * threads) race; calls issued in order on one stream do not.  The first call
+ * on each device looks up the scratch's address (no allocation); make that
+ * first call outside a graph capture.  GQA_ERR_HIP: the lookup failed. */
+int gqa_attn_decode_noalloc(const gqa_layer* layer, const void* q,
+                            const void* k_new, const void* v_new,
+                            const int64_t* pos, int B, float* out,
+                            void* stream);
 
 /* Speculative verification of a drafted block of n (1..GQA_MAX_VERIFY)
  * tokens per sequence at positions pos0[b] .. pos0[b]+n-1, in one pass.

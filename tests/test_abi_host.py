@@ -272,3 +272,25 @@ def test_position_bound(lib):
     assert _decode(lib, L, pos=_pos(top + 1)) == E_POS
     assert _decode(lib, L, pos=_pos(top), ws_bytes=0) == E_WS
     assert _append(lib, L, n=2, pos=_pos(top)) == E_POS
+
+
+def test_decode_noalloc_validation(lib):
+    """The entry point without a workspace validates like gqa_attn_decode
+    before it touches its device scratch (these calls launch nothing)."""
+    L = _layer()   # global, capacity 4096
+
+    def call(layer=L, q=FAKE, kn=None, vn=None, pos=None, B=1, out=FAKE):
+        pos = pos if pos is not None else _pos(*([10] * B))
+        return lib.gqa_attn_decode_noalloc(
+            ctypes.byref(layer) if layer is not None else None, q, kn, vn,
+            pos, B, out, None)
+    assert call(layer=None) == E_ARG
+    assert call(q=None) == E_ARG
+    assert call(out=None) == E_ARG
+    assert call(B=0) == E_ARG
+    assert call(kn=FAKE) == E_ARG            # k_new and v_new go together
+    assert call(kn=FAKE, vn=FAKE + 2) == E_ALN
+    assert call(layer=_layer(kind=7)) == E_UNS
+    assert call(pos=_pos(4096)) == E_POS
+    assert call(pos=_pos(-1)) == E_POS
+    assert _defines()["GQA_NOALLOC_SCRATCH_BYTES"] == 8 << 20

@@ -118,6 +118,20 @@ def test_decode_plans_on_a_full_mi355x(plans):
     assert decode(GLOBAL, 1, 131072, 256)["splits"] == 256
 
 
+def test_noalloc_scratch_holds_every_decode_on_a_full_mi355x(plans):
+    """The no-allocation entry point's 8 MiB scratch holds the partials of
+    every decode call a 256-CU device plans (at most 4.3 MB)."""
+    decode, _ = plans
+    worst = 0
+    for kind in (LOCAL, GLOBAL):
+        for B in range(1, 65):
+            for ctx in (1, 64, 2048, 2049, 4096, 32768, 100000, 131072):
+                keys = min(ctx, W) if kind == LOCAL else ctx
+                worst = max(worst, decode(kind, B, keys, 256)["ws"])
+    assert worst <= 8 << 20
+    assert worst == 2 * 256 * 16 * 130 * 4        # batch 1, 256 splits
+
+
 @pytest.mark.parametrize("cus,xcds", SHAPES)
 def test_block_plans_cover_and_fit(plans, cus, xcds):
     _, block = plans
