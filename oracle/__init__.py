@@ -20,6 +20,9 @@ What it defines, each cited by page and section:
 * :func:`attend_block_together` -- a block of tokens predicted together
   (block-diffusion drafting, section 04 of the shishifenxi.com page): every
   query of the block sees the context and the whole block.
+* :mod:`oracle.fp8` -- an fp8 (E4M3) cache with one scale per token and KV
+  head: the quantiser, the dequantised values and attention over them
+  ("Narrow cache": cache quantisation changes the measured cache use).
 * :func:`expected_cache` -- integer-only cache contents after a sequence of
   appends: global slot = position, local slot = position mod window, latest
   write wins ("Narrow cache": the engine must evict or cyclically reuse stale
@@ -80,6 +83,9 @@ def _configure(lib):
                                        p, p, i64, i64, i64, i64, p, p,
                                        p, ctypes.c_int32]
     lib.gqa_oracle_partial.restype = ctypes.c_int
+    lib.gqa_oracle_attend_kv64.argtypes = [ctypes.POINTER(_Cfg), p, p, i64,
+                                           p, p, i64, i64, p, ctypes.c_int32]
+    lib.gqa_oracle_attend_kv64.restype = ctypes.c_int
     lib.gqa_oracle_rope.argtypes = [p, ctypes.c_int32, ctypes.c_double,
                                     ctypes.c_double, p]
     lib.gqa_oracle_rope.restype = None

@@ -104,6 +104,8 @@ typedef struct {
   const int64_t* qpos;
   const uint16_t* k;
   const uint16_t* v;
+  const double* k64;  /* keys / values given as exact doubles (a quantised */
+  const double* v64;  /* cache, dequantised) instead of bf16 bits, or NULL */
   int64_t kpos0, nk;
   const double* krot; /* [nk][hkv][d] rotated keys when cfg->rope, else NULL */
   int64_t jlo, jhi;   /* extra key restriction for partial sums */
@@ -123,8 +125,12 @@ static void rotate_keys(void* p, int64_t lo, int64_t hi) {
   double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
   for (int64_t r = lo; r < hi; ++r) {
     for (int32_t g = 0; g < hkv; ++g) {
-      const uint16_t* src = a->k + (r * hkv + g) * d;
-      for (int32_t c = 0; c < d; ++c) tmp[c] = widen_bf16(src[c]);
+      if (a->k64) {
+        memcpy(tmp, a->k64 + (r * hkv + g) * d, sizeof(double) * (size_t)d);
+      } else {
+        const uint16_t* src = a->k + (r * hkv + g) * d;
+        for (int32_t c = 0; c < d; ++c) tmp[c] = widen_bf16(src[c]);
+      }
       gqa_oracle_rope(tmp, d, (double)(a->kpos0 + r), a->cfg->theta,
                       (double*)a->krot + (r * hkv + g) * d);
     }
@@ -178,6 +184,8 @@ static void attend_rows(void* p, int64_t lo_item, int64_t hi_item) {
       const double* kr;
       if (a->krot) {
         kr = a->krot + (r * hkv + g) * d;
+      } else if (a->k64) {
+        kr = a->k64 + (r * hkv + g) * d;
       } else {
         const uint16_t* ksrc = a->k + (r * hkv + g) * d;
         for (int32_t c = 0; c < d; ++c) kw[c] = widen_bf16(ksrc[c]);
@@ -194,8 +202,12 @@ static void attend_rows(void* p, int64_t lo_item, int64_t hi_item) {
     for (int64_t t = 0; t < cnt; ++t) {
       const double w = exp(s[t] - mx);
       lsum += w;
-      const uint16_t* vsrc = a->v + ((jlo + t - a->kpos0) * hkv + g) * d;
-      for (int32_t c = 0; c < d; ++c) acc[c] += w * widen_bf16(vsrc[c]);
+      const int64_t vr = ((jlo + t - a->kpos0) * hkv + g) * d;
+      if (a->v64) {
+        for (int32_t c = 0; c < d; ++c) acc[c] += w * a->v64[vr + c];
+      } else {
+        for (int32_t c = 0; c < d; ++c) acc[c] += w * widen_bf16(a->v[vr + c]);
+      }
     }
     double* o = a->out + (n * hq + h) * d;
     if (a->normalise) {
@@ -220,9 +232,10 @@ static int check_cfg(const gqa_oracle_cfg* cfg) {
 
 static int run(const gqa_oracle_cfg* cfg, const uint16_t* q,
                const int64_t* qpos, int64_t nq, const uint16_t* k,
-               const uint16_t* v, int64_t kpos0, int64_t nk, int64_t jlo,
-               int64_t jhi, int32_t normalise, double* out, double* m,
-               double* l, int32_t nthreads) {
+               const uint16_t* v, const double* k64, const double* v64,
+               int64_t kpos0, int64_t nk, int64_t jlo, int64_t jhi,
+               int32_t normalise, double* out, double* m, double* l,
+               int32_t nthreads) {
   if (!check_cfg(cfg) || nq < 0 || nk < 0 || (nq > 0 && (!q || !qpos || !out)))
     return GQA_ORACLE_EARG;
   if (!normalise && nq > 0 && (!m || !l)) return GQA_ORACLE_EARG;
@@ -235,7 +248,7 @@ static int run(const gqa_oracle_cfg* cfg, const uint16_t* q,
     if (hi > lo && (lo < kpos0 || hi > kpos0 + nk)) return GQA_ORACLE_ERANGE;
   }
   if (nq == 0) return GQA_ORACLE_OK;
-  if (nk > 0 && (!k || !v)) return GQA_ORACLE_EARG;
+  if (nk > 0 && (!(k || k64) || !(v || v64))) return GQA_ORACLE_EARG;
 
   attend_ctx a;
   memset(&a, 0, sizeof a);
@@ -244,6 +257,8 @@ static int run(const gqa_oracle_cfg* cfg, const uint16_t* q,
   a.qpos = qpos;
   a.k = k;
   a.v = v;
+  a.k64 = k64;
+  a.v64 = v64;
   a.kpos0 = kpos0;
   a.nk = nk;
   a.jlo = jlo;
@@ -269,8 +284,16 @@ int gqa_oracle_attend(const gqa_oracle_cfg* cfg, const uint16_t* q,
                       const int64_t* qpos, int64_t nq, const uint16_t* k,
                       const uint16_t* v, int64_t kpos0, int64_t nk,
                       double* out, int32_t nthreads) {
-  return run(cfg, q, qpos, nq, k, v, kpos0, nk, INT64_MIN, INT64_MAX, 1, out,
-             NULL, NULL, nthreads);
+  return run(cfg, q, qpos, nq, k, v, NULL, NULL, kpos0, nk, INT64_MIN,
+             INT64_MAX, 1, out, NULL, NULL, nthreads);
+}
+
+int gqa_oracle_attend_kv64(const gqa_oracle_cfg* cfg, const uint16_t* q,
+                           const int64_t* qpos, int64_t nq, const double* k,
+                           const double* v, int64_t kpos0, int64_t nk,
+                           double* out, int32_t nthreads) {
+  return run(cfg, q, qpos, nq, NULL, NULL, k, v, kpos0, nk, INT64_MIN,
+             INT64_MAX, 1, out, NULL, NULL, nthreads);
 }
 
 int gqa_oracle_partial(const gqa_oracle_cfg* cfg, const uint16_t* q,
@@ -278,6 +301,6 @@ int gqa_oracle_partial(const gqa_oracle_cfg* cfg, const uint16_t* q,
                        const uint16_t* v, int64_t kpos0, int64_t nk,
                        int64_t jlo, int64_t jhi, double* m, double* l,
                        double* o, int32_t nthreads) {
-  return run(cfg, q, qpos, nq, k, v, kpos0, nk, jlo, jhi, 0, o, m, l,
-             nthreads);
+  return run(cfg, q, qpos, nq, k, v, NULL, NULL, kpos0, nk, jlo, jhi, 0, o, m,
+             l, nthreads);
 }

@@ -62,6 +62,14 @@ int gqa_oracle_attend(const gqa_oracle_cfg* cfg, const uint16_t* q,
                       const uint16_t* v, int64_t kpos0, int64_t nk,
                       double* out, int32_t nthreads);
 
+/* The same attention over keys and values given as exact doubles instead of
+ * bf16 bits: k, v [nk][hkv][d] (e.g. a quantised cache's dequantised
+ * values).  Everything else as gqa_oracle_attend. */
+int gqa_oracle_attend_kv64(const gqa_oracle_cfg* cfg, const uint16_t* q,
+                           const int64_t* qpos, int64_t nq, const double* k,
+                           const double* v, int64_t kpos0, int64_t nk,
+                           double* out, int32_t nthreads);
+
 /* The same sums restricted to keys with position in [jlo, jhi) (intersected
  * with each query's visible set), left unnormalised:
  *   m[n][h] = max s_j (or -inf when no key is visible),
