@@ -22,7 +22,7 @@ __all__ = [
     "MAX_VERIFY", "attn_verify", "attn_draft_block", "attn_prefill", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
     "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
     "attn_decode", "attn_decode_append", "attn_decode_dev",
-    "attn_decode_noalloc", "workspace_bytes", "workspace", "status_string", "abi_version",
+    "attn_decode_noalloc", "LayerFp8", "kv_append_fp8", "attn_decode_fp8", "workspace_bytes", "workspace", "status_string", "abi_version",
     "library_path", "layer_kind", "NUM_LAYERS",
 ]
 
@@ -55,6 +55,15 @@ class _CLayer(ctypes.Structure):
                 ("capacity", ctypes.c_int64), ("rope_theta", ctypes.c_double),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("seq_stride", ctypes.c_int64)]
+
+
+class _CLayerFp8(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("capacity", ctypes.c_int64), ("rope_theta", ctypes.c_double),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("seq_stride", ctypes.c_int64),
+                ("scale_stride", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -96,6 +105,12 @@ def _load():
                                                ctypes.c_size_t, p]
         lib.gqa_attn_decode_dev.restype = i32
         lib.gqa_attn_decode_dev.argtypes = [L, p, p, p, p, i64, i32, p, p,
+                                            ctypes.c_size_t, p]
+        L8 = ctypes.POINTER(_CLayerFp8)
+        lib.gqa_kv_append_fp8.restype = i32
+        lib.gqa_kv_append_fp8.argtypes = [L8, p, p, p, i32, i32, p]
+        lib.gqa_attn_decode_fp8.restype = i32
+        lib.gqa_attn_decode_fp8.argtypes = [L8, p, p, i32, p, p,
                                             ctypes.c_size_t, p]
         lib.gqa_attn_decode_noalloc.restype = i32
         lib.gqa_attn_decode_noalloc.argtypes = [L, p, p, p, p, i32, p, p]
@@ -163,6 +178,71 @@ class Layer:
     @property
     def c_ref(self):
         return ctypes.byref(self._c)
+
+
+class LayerFp8:
+    """One attention layer's fp8 cache in caller-owned torch tensors: E4M3
+    codes k, v (uint8 [B, capacity, 2, 128]) and one fp32 scale per (token,
+    KV head), k_scale, v_scale (float32 [B, 2, capacity]).  Kinds, capacities
+    and RoPE as :class:`Layer`."""
+
+    def __init__(self, kind, k, v, k_scale, v_scale, rope_theta=None):
+        self.kind = int(kind)
+        self.k, self.v, self.k_scale, self.v_scale = k, v, k_scale, v_scale
+        if rope_theta is None:
+            rope_theta = ROPE_THETA if self.kind == LOCAL else 0.0
+        self.rope_theta = float(rope_theta)
+        assert k.shape == v.shape and k.dim() == 4 and k.dtype == torch.uint8
+        assert k_scale.shape == v_scale.shape and k_scale.dim() == 3
+        assert k_scale.dtype == torch.float32
+        self.batch, self.capacity = int(k.shape[0]), int(k.shape[1])
+        if tuple(k_scale.shape) != (self.batch, HKV, self.capacity) or \
+                k_scale.stride(1) != self.capacity or k_scale.stride(2) != 1:
+            raise ValueError("scales must be [B, 2, capacity] with unit stride")
+        if k.stride(0) != v.stride(0) or k_scale.stride(0) != v_scale.stride(0):
+            raise ValueError("k and v (and their scales) share their strides")
+        self._c = _CLayerFp8(self.kind, WINDOW if self.kind == LOCAL else 0,
+                             self.capacity, self.rope_theta, k.data_ptr(),
+                             v.data_ptr(), k_scale.data_ptr(),
+                             v_scale.data_ptr(), int(k.stride(0)),
+                             int(k_scale.stride(0)))
+
+    @classmethod
+    def allocate(cls, kind, batch, capacity=None, device="cuda", fill=0):
+        """Codes filled with the byte ``fill``, scales with 0."""
+        if capacity is None:
+            capacity = WINDOW if kind == LOCAL else MAX_CONTEXT
+        shape = (batch, capacity, HKV, D)
+        k = torch.full(shape, fill, dtype=torch.uint8, device=device)
+        v = torch.full(shape, fill, dtype=torch.uint8, device=device)
+        ks = torch.zeros((batch, HKV, capacity), dtype=torch.float32,
+                         device=device)
+        vs = torch.zeros_like(ks)
+        return cls(kind, k, v, ks, vs)
+
+    @property
+    def c_ref(self):
+        return ctypes.byref(self._c)
+
+
+def kv_append_fp8(layer: LayerFp8, k_new, v_new, pos0, stream=None):
+    """Quantise n new tokens per sequence (k_new, v_new: bf16 [B, n, 2, 128])
+    into the layer's fp8 cache at positions pos0[b] .. pos0[b]+n-1."""
+    B, n = int(k_new.shape[0]), int(k_new.shape[1])
+    kp = _dev(k_new, torch.bfloat16, (B, n, HKV, D), "k_new")
+    vp = _dev(v_new, torch.bfloat16, (B, n, HKV, D), "v_new")
+    rc = _load().gqa_kv_append_fp8(layer.c_ref, kp, vp, _positions(pos0, B),
+                                   B, n, _stream(stream))
+    if rc != 0:
+        raise GqaError(rc, "gqa_kv_append_fp8")
+
+
+def attn_decode_fp8(layer: LayerFp8, q, pos, out=None, ws=None, stream=None):
+    """One decode step over an fp8 cache: q bf16 [B, 32, 128] at host
+    positions pos (the token already appended).  Returns fp32
+    [B, 32, 128]."""
+    return _decode_common(_load().gqa_attn_decode_fp8, "gqa_attn_decode_fp8",
+                          layer, q, pos, out, ws, stream)
 
 
 def _stream(stream):

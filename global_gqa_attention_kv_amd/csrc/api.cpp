@@ -109,15 +109,20 @@ int gqa_kv_append(const gqa_layer* layer, const void* k_new, const void* v_new,
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+// Decode on a bf16 cache (layer) or an fp8 cache (layer8, with layer null;
+// no fused append, host positions only).
 static int decode_impl(const gqa_layer* layer, const void* q,
                        const void* k_new, const void* v_new,
                        const int64_t* pos, int B, float* out, void* ws,
                        size_t ws_bytes, void* stream,
                        const int64_t* pos_dev = nullptr,
-                       int64_t max_pos = 0, bool noalloc = false) {
+                       int64_t max_pos = 0, bool noalloc = false,
+                       const gqa_layer_fp8* layer8 = nullptr) {
   int64_t max_keys = 0;
   int rc;
-  if (pos_dev) {
+  if (layer8) {
+    rc = check_decode_fp8(layer8, q, pos, B, out, &max_keys);
+  } else if (pos_dev) {
     // the kernels read the positions; the host checks the bound they are
     // held to, exactly as it checks a position
     if ((uintptr_t)pos_dev & 7u) return GQA_ERR_MISALIGNED;
@@ -134,8 +139,10 @@ static int decode_impl(const gqa_layer* layer, const void* q,
     if (((uintptr_t)k_new & 15u) || ((uintptr_t)v_new & 15u))
       return GQA_ERR_MISALIGNED;
   }
+  const int32_t kind = layer8 ? layer8->kind : layer->kind;
+  const double theta = layer8 ? layer8->rope_theta : layer->rope_theta;
   const DeviceShape dev = current_device_shape();
-  const DecodePlan plan = plan_decode(layer->kind, B, max_keys, dev);
+  const DecodePlan plan = plan_decode(kind, B, max_keys, dev);
   if (plan.splits > kMaxSplits) return GQA_ERR_UNSUPPORTED;
   const size_t need = decode_ws_bytes(B, plan);
   if (noalloc) {
@@ -150,33 +157,45 @@ static int decode_impl(const gqa_layer* layer, const void* q,
   if (ws_bytes < need) return GQA_ERR_WS_TOO_SMALL;
   DecodeParams p;
   memset(&p, 0, sizeof p);
-  p.k = static_cast<const uint16_t*>(layer->k);
-  p.k_mut = static_cast<uint16_t*>(layer->k);
-  p.v = static_cast<const uint16_t*>(layer->v);
-  p.v_mut = static_cast<uint16_t*>(layer->v);
-  p.k_new = static_cast<const uint16_t*>(k_new);
-  p.v_new = static_cast<const uint16_t*>(v_new);
+  if (layer8) {
+    p.k8 = static_cast<const uint8_t*>(layer8->k);
+    p.v8 = static_cast<const uint8_t*>(layer8->v);
+    p.k_scale = layer8->k_scale;
+    p.v_scale = layer8->v_scale;
+    p.seq_stride = layer8->seq_stride;
+    p.scale_stride = layer8->scale_stride;
+    p.capacity = layer8->capacity;
+  } else {
+    p.k = static_cast<const uint16_t*>(layer->k);
+    p.k_mut = static_cast<uint16_t*>(layer->k);
+    p.v = static_cast<const uint16_t*>(layer->v);
+    p.v_mut = static_cast<uint16_t*>(layer->v);
+    p.k_new = static_cast<const uint16_t*>(k_new);
+    p.v_new = static_cast<const uint16_t*>(v_new);
+    p.seq_stride = layer->seq_stride;
+    p.capacity = layer->capacity;
+  }
   p.q = static_cast<const uint32_t*>(q);
   p.part = static_cast<float*>(ws);
   p.out = out;
-  p.seq_stride = layer->seq_stride;
   p.scale_log2 = (float)(1.0 / sqrt((double)kD) * 1.4426950408889634);
   p.splits = plan.splits;
   p.tiles_per_split = plan.tiles_per_split;
   p.units = B * kHkv * plan.splits;
   p.xcds = dev.xcds;
-  const bool local = layer->kind == GQA_LOCAL;
+  const bool local = kind == GQA_LOCAL;
   if (local) {
     // revolutions per position of frequency c: theta^(-c/64) / (2 pi),
     // evaluated in double and rounded once.
     for (int c = 0; c < kD / 2; ++c)
-      p.rope_rev[c] = (float)(pow(layer->rope_theta, -(double)c / (kD / 2)) /
+      p.rope_rev[c] = (float)(pow(theta, -(double)c / (kD / 2)) /
                               (2.0 * 3.14159265358979323846));
   }
   p.pos_dev = pos_dev;
   p.max_pos = max_pos;
   for (int b = 0; b < B; ++b) p.pos[b] = pos_dev ? max_pos : pos[b];
-  hipError_t e = launch_decode(p, plan, local, B, (hipStream_t)stream);
+  hipError_t e = launch_decode(p, plan, local, layer8 != nullptr, B,
+                               (hipStream_t)stream);
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
@@ -203,6 +222,37 @@ int gqa_attn_decode_dev(const gqa_layer* layer, const void* q,
   if (!pos_dev) return GQA_ERR_INVALID_ARG;
   return decode_impl(layer, q, k_new, v_new, nullptr, B, out, ws, ws_bytes,
                      stream, pos_dev, max_pos);
+}
+
+int gqa_kv_append_fp8(const gqa_layer_fp8* layer, const void* k_new,
+                      const void* v_new, const int64_t* pos0, int B, int n,
+                      void* stream) {
+  int rc = check_append_fp8(layer, k_new, v_new, pos0, B, n);
+  if (rc != GQA_OK) return rc;
+  AppendFp8Params p;
+  memset(&p, 0, sizeof p);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k = static_cast<uint8_t*>(layer->k);
+  p.v = static_cast<uint8_t*>(layer->v);
+  p.k_scale = layer->k_scale;
+  p.v_scale = layer->v_scale;
+  p.seq_stride = layer->seq_stride;
+  p.scale_stride = layer->scale_stride;
+  p.capacity = layer->capacity;
+  p.n = n;
+  p.local = layer->kind == GQA_LOCAL;
+  p.first = (p.local && n > kW) ? n - kW : 0;
+  for (int b = 0; b < B; ++b) p.pos0[b] = pos0[b];
+  hipError_t e = launch_kv_append_fp8(p, B, n - p.first, (hipStream_t)stream);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_attn_decode_fp8(const gqa_layer_fp8* layer, const void* q,
+                        const int64_t* pos, int B, float* out, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return decode_impl(nullptr, q, nullptr, nullptr, pos, B, out, ws, ws_bytes,
+                     stream, nullptr, 0, false, layer);
 }
 
 int gqa_attn_decode_noalloc(const gqa_layer* layer, const void* q,

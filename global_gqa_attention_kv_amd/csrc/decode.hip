@@ -107,6 +107,28 @@ __device__ __forceinline__ void dma16(const uint16_t* base, uint32_t off,
       : "v"(off), "s"(base), "s"(lds)
       : "memory");
 }
+// Direct-to-LDS load of 4 bytes per lane (lane l's word lands at lds + 4 l).
+__device__ __forceinline__ void dma4(const float* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// Two E4M3 codes (the lower or upper half of w, first code in the lower
+// byte) as a bf16 pair, exactly (scale 1).
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // Maximum and sum over the 16 lanes of a DPP row.
 __device__ __forceinline__ float row_max(float x) {
 #pragma unroll
@@ -137,7 +159,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the wave: heads 4 r .. 4 r + 3) -- so no wave reads another's rows and
 // the tile loop needs no barrier; the four waves' sums are combined once at
 // the end.
-template <int WAVES, int HPW, int KR, int VR, bool LOCAL, bool KSPLIT = false>
+//
+// F8: the cache holds E4M3 codes plus one fp32 scale per (token, KV head).
+// The rings then hold code tiles (64 rows of 128 bytes) and each row's scale;
+// once its rows have landed, each wave dequantises them (code x scale, to
+// bf16) into a bf16 staging tile laid out as the bf16 rings are, and the
+// products read the staging tile.
+template <int WAVES, int HPW, int KR, int VR, bool LOCAL, bool KSPLIT = false,
+          bool F8 = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     const DecodeParams p) {
   constexpr int NT = 64 * WAVES;
@@ -152,7 +181,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   static_assert(KR == VR || KR == VR + 1, "K at most one tile further ahead");
   static_assert(!KSPLIT || (!LOCAL && WAVES == 4 && HPW == kGroup && KR > 1),
                 "key split: global layers, four waves of 16 keys, all heads");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[(KR + VR) * kTileBytes];
+  // F8 LDS: code rings (8 KB a tile), per-wave scale slots (64 words each),
+  // then the bf16 staging tiles of K and V
+  constexpr int kCodeTile = kDecTile * kD;                 // 8 KB
+  constexpr int kScaleSlot = WAVES * 256;                  // bytes per slot
+  constexpr int kF8Bytes = (KR + VR) * (kCodeTile + kScaleSlot) +
+                           2 * kTileBytes;
+  constexpr int kSmem = F8 ? kF8Bytes : (KR + VR) * kTileBytes;
+  static_assert(!F8 || RPW % 8 == 0, "whole 1 KB code loads per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -203,8 +240,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   // The call appends the query's own token: one workgroup writes it to its
   // slot, which no other workgroup reads in this launch (they take that key
   // from k_new / v_new).
-  if (use_new && g == 0 && hg == 0 && has_keys && new_key / span == split &&
-      tid < 64) {
+  if (!F8 && use_new && g == 0 && hg == 0 && has_keys &&
+      new_key / span == split && tid < 64) {
     const bool is_v = tid >= 32;
     const int chunk = tid & 31;
     const uint16_t* src = (is_v ? p.v_new : p.k_new) +
@@ -222,6 +259,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   const int ntiles = (k_end - k_begin + kDecTile - 1) / kDecTile;
   const uint16_t* Kb = p.k + (int64_t)b * p.seq_stride + g * kD;
   const uint16_t* Vb = p.v + (int64_t)b * p.seq_stride + g * kD;
+  // F8: codes (seq_stride in bytes) and scales of this (sequence, KV head)
+  const uint8_t* K8b = p.k8 + (int64_t)b * p.seq_stride + g * kD;
+  const uint8_t* V8b = p.v8 + (int64_t)b * p.seq_stride + g * kD;
+  const float* KSb = p.k_scale + (int64_t)b * p.scale_stride + g * p.capacity;
+  const float* VSb = p.v_scale + (int64_t)b * p.scale_stride + g * p.capacity;
   const uint16_t* Kn = p.k_new + (int64_t)b * kTokenElems + g * kD;
   const uint16_t* Vn = p.v_new + (int64_t)b * kTokenElems + g * kD;
   // first head of this lane's row: the wave's heads, or (KSPLIT) row r's
@@ -304,6 +346,98 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     issue(t, std::true_type{}, vbase + VS * kTileBytes);
   };
 
+  // F8: code slots of K then V, their scale slots (wave w's 256 bytes each),
+  // then the bf16 staging tiles.  Lane l of wave w loads code chunk l % 8 of
+  // row RPW w + 8 i + l / 8 (a row is 128 codes of one KV head) and the scale
+  // of row RPW w + l % RPW.
+  constexpr int LPT8 = RPW / 8;                 // 1 KB code loads per tile
+  const uint32_t k8base = lds_base;
+  const uint32_t v8base = k8base + KR * kCodeTile;
+  const uint32_t ksbase = v8base + VR * kCodeTile;
+  const uint32_t vsbase = ksbase + KR * kScaleSlot;
+  const uint32_t stk = vsbase + VR * kScaleSlot;  // staging K, bf16
+  const uint32_t stv = stk + kTileBytes;          // staging V, bf16
+  const int crow = lane >> 3, cch = lane & 7;
+  const int srow = RPW * w + lane % RPW;
+  auto issue8 = [&](int t, auto IS_V, uint32_t lds, uint32_t slds) {
+    const uint8_t* base = IS_V ? V8b : K8b;
+    const float* sb = IS_V ? VSb : KSb;
+    const int kb = k_begin + t * kDecTile;
+    const int64_t slot0 = slot_of(j_first + kb, LOCAL);
+    lds = __builtin_amdgcn_readfirstlane(lds + w * RPW * kD);
+    slds = __builtin_amdgcn_readfirstlane(slds + w * 256);
+    if (kb + kDecTile <= k_end && (!LOCAL || slot0 + kDecTile <= kW)) {
+      const uint8_t* tb = base + slot0 * (kHkv * kD);
+#pragma unroll
+      for (int i = 0; i < LPT8; ++i)
+        dma16(reinterpret_cast<const uint16_t*>(tb),
+              (uint32_t)((RPW * w + 8 * i + crow) * (kHkv * kD) + cch * 16),
+              lds + i * 1024);
+      dma4(sb + slot0 + srow, slds);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT8; ++i) {
+        const int key = min(kb + RPW * w + 8 * i + crow, k_end - 1);
+        const int64_t slot = slot_of(j_first + key, LOCAL);
+        dma16(reinterpret_cast<const uint16_t*>(base + slot * (kHkv * kD) +
+                                                cch * 16),
+              lds + i * 1024);
+      }
+      dma4(sb + slot_of(j_first + min(kb + srow, k_end - 1), LOCAL), slds);
+    }
+  };
+  auto issue8_k = [&](int t, auto KS) {
+    issue8(t, std::false_type{}, k8base + KS * kCodeTile,
+           ksbase + KS * kScaleSlot);
+  };
+  auto issue8_v = [&](int t, auto VS) {
+    issue8(t, std::true_type{}, v8base + VS * kCodeTile,
+           vsbase + VS * kScaleSlot);
+  };
+  // loads one tile issue puts in flight per wave (the ring waits count them)
+  constexpr int LPI = F8 ? LPT8 + 1 : LPT;
+  // Wave w turns its own rows of the landed code tiles into bf16 codes in
+  // the staging tiles (exact: every E4M3 value is a bf16 value), in the
+  // swizzled layouts the products read; the scales are applied to the
+  // scores (K) and the weights (V).
+  auto dequant = [&](auto KS, auto VS) {
+    static_for<0, LPT8>([&](auto I) {
+      const int row = RPW * w + 8 * I + crow;
+      static_for<0, 2>([&](auto IV) {
+        const uint32_t src = (IV ? v8base + VS * kCodeTile
+                                 : k8base + KS * kCodeTile) +
+                             row * kD + cch * 16;
+        const u32x4_t c = *reinterpret_cast<const lds_u32x4_t*>(src);
+        u32x4_t lo, hi;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          lo[2 * e] = cvt_fp8x2_bf16<false>(c[e]);
+          lo[2 * e + 1] = cvt_fp8x2_bf16<true>(c[e]);
+          hi[2 * e] = cvt_fp8x2_bf16<false>(c[e + 2]);
+          hi[2 * e + 1] = cvt_fp8x2_bf16<true>(c[e + 2]);
+        }
+        const int swz = IV ? 2 * (row & 7) : (row & 15);
+        const uint32_t dst = (IV ? stv : stk) + row * 256;
+        *reinterpret_cast<lds_u32x4_t*>(dst + (((2 * cch) ^ swz) << 4)) = lo;
+        *reinterpret_cast<lds_u32x4_t*>(dst + (((2 * cch + 1) ^ swz) << 4)) =
+            hi;
+      });
+    });
+  };
+  // scale of key k of the landed tile in K slot KS (V slot VS)
+  auto kscale = [&](int k, auto KS) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+        ksbase + KS * kScaleSlot + (k / RPW) * 256 + 4 * (k % RPW));
+  };
+  auto vscale = [&](int k, auto VS) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+        vsbase + VS * kScaleSlot + (k / RPW) * 256 + 4 * (k % RPW));
+  };
+  // the K tile the products (and the local rotation) read
+  auto ktile = [&](auto KS) -> uint32_t {
+    return F8 ? stk : lds_base + KS * kTileBytes;
+  };
+
   float m[HW], lsum[HW], o[HW][8];
 #pragma unroll
   for (int hl = 0; hl < HW; ++hl) {
@@ -327,15 +461,22 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   // KSPLIT: key 16 w + jl in the products, V rows 16 w .. of every row
   const int krow = KSPLIT ? 16 * w + jl : lane;
   const int vgrp = KSPLIT ? w : kg;
+  const uint32_t kread = F8 ? stk : lds_base, vread = F8 ? stv : vbase;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) krd[c] = lds_base + krow * 256 + ((c ^ jl) << 4);
+  for (int c = 0; c < 16; ++c) krd[c] = kread + krow * 256 + ((c ^ jl) << 4);
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    vrd[e] = vbase + (16 * vgrp + je) * 256 + 32 * (e ^ je) + 8 * ja;
+    vrd[e] = vread + (16 * vgrp + je) * 256 + 32 * (e ^ je) + 8 * ja;
 
   auto consume = [&](int t, auto KS, auto VS) {
-    constexpr uint32_t so = KS * kTileBytes;
-    constexpr uint32_t vso = VS * kTileBytes;
+    constexpr uint32_t so = F8 ? 0 : KS * kTileBytes;
+    constexpr uint32_t vso = F8 ? 0 : VS * kTileBytes;
+    // F8: the scales of this lane's key (the one whose scores it holds)
+    float ksc = 1.0f, vsc = 1.0f;
+    if constexpr (F8) {
+      ksc = kscale(krow, KS) * p.scale_log2;
+      vsc = vscale(krow, VS);
+    }
     // ---- scores: lane = key of this tile (KSPLIT: key krow); the query
     // word of (head hl, pair pr) is broadcast from lane hl * LPH + pr / PPL
     // of the lane's row.  The lane's K row
@@ -410,7 +551,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
       float a = acc[hl][0];
 #pragma unroll
       for (int k = 1; k < NACC; ++k) a += acc[hl][k];
-      s2[hl] = valid ? a * p.scale_log2 : -INFINITY;
+      s2[hl] = valid ? a * (F8 ? ksc : p.scale_log2) : -INFINITY;
       need |= s2[hl] > m[hl] + kTau;
     }
     if (__any(need)) {
@@ -432,8 +573,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     uint32_t pk[HW];
 #pragma unroll
     for (int hl = 0; hl < HW; ++hl) {
-      const uint32_t pb = to_bf16(fast_exp2(s2[hl] - m[hl]));
-      lsum[hl] += __builtin_bit_cast(float, pb << 16);
+      uint32_t pb;
+      if constexpr (F8) {
+        // the weight times the key's V scale goes into P.V; the
+        // denominator sums the weights themselves
+        const float pw = fast_exp2(s2[hl] - m[hl]);
+        lsum[hl] += pw;
+        pb = to_bf16(pw * vsc);
+      } else {
+        pb = to_bf16(fast_exp2(s2[hl] - m[hl]));
+        lsum[hl] += __builtin_bit_cast(float, pb << 16);
+      }
       // lanes 2i take lane 2i + 1's weight (quad_perm [1, 1, 3, 3])
       const uint32_t nb = __builtin_amdgcn_mov_dpp((int)pb, 0xF5, 0xF, 0xF, false);
       pk[hl] = pb | (nb << 16);
@@ -494,10 +644,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     for (int i = 0; i < RIT; ++i) {
       const int u = tid + i * NT, row = u >> 3, cp = u & 7;
       lds_u32x4_t* lo = reinterpret_cast<lds_u32x4_t*>(
-          lds_base + SLOT * kTileBytes + row * 256 + ((cp ^ (row & 15)) << 4));
+          ktile(SLOT) + row * 256 + ((cp ^ (row & 15)) << 4));
       lds_u32x4_t* hi = reinterpret_cast<lds_u32x4_t*>(
-          lds_base + SLOT * kTileBytes + row * 256 +
-          (((cp + 8) ^ (row & 15)) << 4));
+          ktile(SLOT) + row * 256 + (((cp + 8) ^ (row & 15)) << 4));
       u32x4_t a = *lo, c = *hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -514,14 +663,31 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
   };
 
   constexpr auto C0 = std::integral_constant<int, 0>{};
+  // after a wave's dequantisation: its LDS writes are complete before any
+  // read of the staging tiles (KSPLIT: the wave reads only its own rows)
+  auto dequant_done = [&]() {
+    if constexpr (KSPLIT)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    else
+      __syncthreads();
+  };
   if constexpr (KR == 1) {
     // one tile per workgroup (the planner guarantees it): load, wait, use
     if (ntiles > 0) {
-      issue_k(0, C0);
-      issue_v(0, C0);
+      if constexpr (F8) {
+        issue8_k(0, C0);
+        issue8_v(0, C0);
+      } else {
+        issue_k(0, C0);
+        issue_v(0, C0);
+      }
       if constexpr (LOCAL) rope_angles(0);
       wait_vmcnt<0>();
       __syncthreads();
+      if constexpr (F8) {
+        dequant(C0, C0);
+        dequant_done();
+      }
       if constexpr (LOCAL) {
         rope_tile(C0);
         __syncthreads();
@@ -534,14 +700,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     // steps -(KR - 1) .. -1 would have.
     constexpr int DK = KR - 1, DV = VR - 1;
     constexpr int PER = KR == VR ? KR : KR * VR;  // slot pattern period
+    auto load_k = [&](int t, auto KS) {
+      if constexpr (F8) issue8_k(t, KS); else issue_k(t, KS);
+    };
+    auto load_v = [&](int t, auto VS) {
+      if constexpr (F8) issue8_v(t, VS); else issue_v(t, VS);
+    };
     static_for<0, DK>([&](auto I) {
       constexpr int s0 = I - DK;
       if constexpr (s0 + DV >= 0) {
         if (s0 + DV < ntiles)
-          issue_v(s0 + DV, std::integral_constant<int, (s0 + DV) % VR>{});
+          load_v(s0 + DV, std::integral_constant<int, (s0 + DV) % VR>{});
       }
       if (s0 + DK < ntiles)
-        issue_k(s0 + DK, std::integral_constant<int, (s0 + DK) % KR>{});
+        load_k(s0 + DK, std::integral_constant<int, (s0 + DK) % KR>{});
     });
     for (int t0 = 0; t0 < ntiles; t0 += PER) {
       static_for<0, PER>([&](auto S) {
@@ -552,14 +724,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
           // issued after V of tile t is outstanding; the barrier publishes
           // every wave's rows and frees the slots of tile t - 1
           if (DK > DV && t + 1 < ntiles)
-            wait_vmcnt<LPT>();
+            wait_vmcnt<LPI>();
           else
             wait_vmcnt<0>();
           if constexpr (!KSPLIT) __syncthreads();
           if (t + DV < ntiles)
-            issue_v(t + DV, std::integral_constant<int, (S + DV) % VR>{});
+            load_v(t + DV, std::integral_constant<int, (S + DV) % VR>{});
           if (t + DK < ntiles)
-            issue_k(t + DK, std::integral_constant<int, (S + DK) % KR>{});
+            load_k(t + DK, std::integral_constant<int, (S + DK) % KR>{});
+          if constexpr (F8) {
+            dequant(std::integral_constant<int, S % KR>{},
+                    std::integral_constant<int, S % VR>{});
+            dequant_done();
+          }
           if constexpr (LOCAL) {
             rope_tile(std::integral_constant<int, S % KR>{});
             __syncthreads();
@@ -739,28 +916,37 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
 }
 
-}  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
-                         bool local, int B, hipStream_t s) {
+template <bool F8>
+hipError_t launch_split(const DecodeParams& p, const DecodePlan& plan,
+                        bool local, hipStream_t s) {
   if (local && plan.heads_per_wg == kLocalSmallHeads) {
     // small batches: 4 workgroups (head groups) share each tile
     constexpr int HG = kGroup / kLocalSmallHeads;
     const int grid = (p.units + p.xcds - 1) / p.xcds * p.xcds * HG;
     if (p.tiles_per_split != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(
-        (decode_split_kernel<kLocalSmallWaves, kLocalSmallHeads, 1, 1, true>),
-        dim3(grid), dim3(64 * kLocalSmallWaves), 0, s, p);
+    hipLaunchKernelGGL((decode_split_kernel<kLocalSmallWaves, kLocalSmallHeads,
+                                            1, 1, true, false, F8>),
+                       dim3(grid), dim3(64 * kLocalSmallWaves), 0, s, p);
   } else if (local) {
-    hipLaunchKernelGGL((decode_split_kernel<kLocalWaves, kGroup, 2, 2, true>),
-                       dim3(p.units), dim3(64 * kLocalWaves), 0, s, p);
+    hipLaunchKernelGGL(
+        (decode_split_kernel<kLocalWaves, kGroup, 2, 2, true, false, F8>),
+        dim3(p.units), dim3(64 * kLocalWaves), 0, s, p);
   } else {
     hipLaunchKernelGGL(
         (decode_split_kernel<kGlobalWaves, kGroup, kGlobalKRing,
-                             kGlobalVRing, false, true>),
+                             kGlobalVRing, false, true, F8>),
         dim3(p.units), dim3(64 * kGlobalWaves), 0, s, p);
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
+                         bool local, bool fp8, int B, hipStream_t s) {
+  hipError_t e = fp8 ? launch_split<true>(p, plan, local, s)
+                     : launch_split<false>(p, plan, local, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(B * kHq * 4), dim3(256), 0, s,
                      p, plan.heads_per_wg);

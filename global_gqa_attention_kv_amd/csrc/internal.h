@@ -27,6 +27,27 @@ struct AppendParams {
 hipError_t launch_kv_append(const AppendParams& p, int B, int count,
                             hipStream_t s);
 
+// Append to an fp8 cache: the new bf16 tokens are quantised to E4M3 with one
+// scale per (token, KV head) (kv_append.hip).
+struct AppendFp8Params {
+  const uint16_t* k_new;   // [B][n][2][128] bf16
+  const uint16_t* v_new;
+  uint8_t* k;              // code cache base
+  uint8_t* v;
+  float* k_scale;          // scales [B][2][capacity]
+  float* v_scale;
+  int64_t seq_stride;      // bytes between sequences of the codes
+  int64_t scale_stride;    // floats between sequences of the scales
+  int64_t capacity;
+  int32_t n;
+  int32_t first;
+  int32_t local;
+  int32_t pad_;
+  int64_t pos0[kMaxBatch];
+};
+hipError_t launch_kv_append_fp8(const AppendFp8Params& p, int B, int count,
+                                hipStream_t s);
+
 // ---------------------------------------------------------------- decode
 // Global-layer decode: waves per workgroup (each takes 16 keys of every
 // tile for all 16 query heads) and K and V tile slots in its LDS ring (16 KB
@@ -65,10 +86,17 @@ struct DecodeParams {
   float rope_rev[kD / 2];  // local: theta^(-c/64) / (2 pi), revolutions per position
   const int64_t* pos_dev;  // device positions [B] (read instead of pos), or null
   int64_t max_pos;         // with pos_dev: positions above it are not attended
+  // fp8 caches (E4M3 codes plus one fp32 scale per token and KV head)
+  const uint8_t* k8;       // codes, sequence b at byte b * seq_stride
+  const uint8_t* v8;
+  const float* k_scale;    // scales [B][2][capacity]
+  const float* v_scale;
+  int64_t scale_stride;    // floats between sequences of the scales
+  int64_t capacity;        // slots per sequence (KV-head stride of the scales)
   int64_t pos[kMaxBatch];
 };
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan,
-                         bool local, int B, hipStream_t s);
+                         bool local, bool fp8, int B, hipStream_t s);
 
 // Device address of the current device's copy of the no-allocation scratch
 // (kNoAllocScratchBytes), looked up on the first call on each device; null

@@ -18,6 +18,13 @@ int check_append(const gqa_layer* L, const void* k_new, const void* v_new,
 int check_decode(const gqa_layer* L, const void* q, const int64_t* pos, int B,
                  const float* out, int64_t* max_keys);
 
+// The same for layers whose cache is fp8 codes plus scales.
+int check_layer_fp8(const gqa_layer_fp8* L);
+int check_append_fp8(const gqa_layer_fp8* L, const void* k_new,
+                     const void* v_new, const int64_t* pos0, int B, int n);
+int check_decode_fp8(const gqa_layer_fp8* L, const void* q, const int64_t* pos,
+                     int B, const float* out, int64_t* max_keys);
+
 // Verification (verify = true, n <= 16) or prefill of a block of n tokens.
 // On success *max_keys is the largest key count any query of the call sees.
 int check_block(const gqa_layer* L, const void* q, const void* k_blk,

@@ -246,6 +246,61 @@ int gqa_attn_prefill(const gqa_layer* layer, const void* q,
                      const int64_t* pos0, int B, int n, void* out, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------- fp8 caches
+ * A layer's cache may instead hold 8-bit codes: OCP FP8 E4M3 (sign, 4-bit
+ * exponent with bias 7, 3-bit mantissa, largest finite value 448) plus one
+ * fp32 scale per (token, KV head), separately for K and for V -- 528 bytes
+ * per token per layer instead of 1024.  A head's 128 values x are stored as
+ * s = amax / 448 (amax: their largest magnitude) and
+ * code = round-to-nearest-even(clamp(x / s, -448, 448)), both divisions
+ * rounded to nearest in fp32; amax = 0 stores s = 0 and zero codes.
+ * Attention reads the values code * s.
+ * Pages: runtimewire.com "Narrow cache" (cache quantisation is among the
+ * factors that change how much memory the cache really takes; the pages
+ * give no format -- this one is the library's reading).
+ *
+ * One attention layer's fp8 cache, owned by the caller.
+ *   kind, window, capacity, rope_theta  as in gqa_layer
+ *   k, v          device uint8 codes [B][capacity][2][128]; sequence b starts
+ *                 at byte b * seq_stride
+ *   k_scale, v_scale  device fp32 scales [B][2][capacity]; sequence b starts
+ *                 at element b * scale_stride, KV head g at + g * capacity
+ *   seq_stride    bytes between sequences, >= capacity * 256, multiple of 16
+ *   scale_stride  floats between sequences, >= 2 * capacity
+ * All four buffers 16-byte aligned. */
+typedef struct gqa_layer_fp8 {
+  int32_t kind;
+  int32_t window;
+  int64_t capacity;
+  double rope_theta;
+  void* k;
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  int64_t seq_stride;
+  int64_t scale_stride;
+} gqa_layer_fp8;
+
+/* gqa_kv_append for an fp8 cache: quantises n new bf16 tokens per sequence
+ * (k_new, v_new: [B][n][2][128] bf16) as above and writes their codes and
+ * scales to the slots gqa_kv_append would use (global: position; local:
+ * position mod 2048, only the last 2048 tokens of a block).  Bit-exact:
+ * the codes and scales are fully determined by the bf16 inputs.  Errors as
+ * gqa_kv_append. */
+int gqa_kv_append_fp8(const gqa_layer_fp8* layer, const void* k_new,
+                      const void* v_new, const int64_t* pos0, int B, int n,
+                      void* stream);
+
+/* gqa_attn_decode over an fp8 cache: one query token per sequence at
+ * pos[b] (its own K/V already appended), attending to the dequantised keys
+ * and values (global: positions 0..pos[b]; local: pos[b]-2047..pos[b]
+ * through the ring, with RoPE).  q [B][32][128] bf16, out [B][32][128]
+ * fp32; workspace and errors as gqa_attn_decode
+ * (gqa_workspace_bytes(GQA_OP_DECODE, kind, B, 1, max pos + 1)). */
+int gqa_attn_decode_fp8(const gqa_layer_fp8* layer, const void* q,
+                        const int64_t* pos, int B, float* out, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* Workspace bytes an operation needs for any call on a layer of `kind` with
  * batch B, n tokens per sequence and context (keys visible to the last
  * query) at most max_ctx.  Returns 0 for invalid arguments. */

@@ -294,3 +294,65 @@ def test_decode_noalloc_validation(lib):
     assert call(pos=_pos(4096)) == E_POS
     assert call(pos=_pos(-1)) == E_POS
     assert _defines()["GQA_NOALLOC_SCRATCH_BYTES"] == 8 << 20
+
+
+def _layer8(kind=ga.GLOBAL, capacity=4096, k=FAKE, v=FAKE + (1 << 30),
+            ks=FAKE + (2 << 30), vs=FAKE + (3 << 30), stride=None,
+            sstride=None, theta=None, window=None):
+    if kind == ga.LOCAL and capacity == 4096:
+        capacity = ga.WINDOW
+    if window is None:
+        window = ga.WINDOW if kind == ga.LOCAL else 0
+    if theta is None:
+        theta = 10000.0 if kind == ga.LOCAL else 0.0
+    return ga._CLayerFp8(kind, window, capacity, theta, k, v, ks, vs,
+                         capacity * 256 if stride is None else stride,
+                         2 * capacity if sstride is None else sstride)
+
+
+def test_fp8_append_validation(lib):
+    def call(L, B=1, n=1, kn=FAKE, vn=FAKE, pos=None):
+        pos = pos if pos is not None else _pos(*([0] * B))
+        return lib.gqa_kv_append_fp8(ctypes.byref(L) if L is not None else
+                                     None, kn, vn, pos, B, n, None)
+    L = _layer8()
+    assert call(None) == E_ARG
+    assert call(L, kn=None) == E_ARG
+    assert call(L, B=0) == E_ARG
+    assert call(L, n=0) == E_ARG
+    assert call(_layer8(ks=0)) == E_ARG
+    assert call(_layer8(vs=0)) == E_ARG
+    assert call(_layer8(k=0)) == E_ARG
+    assert call(_layer8(kind=4)) == E_UNS
+    assert call(_layer8(kind=ga.LOCAL, capacity=4096 * 2)) == E_UNS
+    assert call(_layer8(kind=ga.LOCAL, theta=0.0)) == E_UNS
+    assert call(_layer8(stride=4096 * 256 - 16)) == E_ARG
+    assert call(_layer8(sstride=2 * 4096 - 4)) == E_ARG
+    assert call(_layer8(stride=4096 * 256 + 8)) == E_ALN
+    assert call(_layer8(ks=FAKE + 4)) == E_ALN
+    assert call(_layer8(v=FAKE + 8)) == E_ALN
+    assert call(L, kn=FAKE + 2) == E_ALN
+    assert call(L, pos=_pos(-1)) == E_POS
+    assert call(L, n=2, pos=_pos(4095)) == E_POS
+
+
+def test_fp8_decode_validation(lib):
+    def call(L, B=1, q=FAKE, out=FAKE, pos=None, ws=FAKE, ws_bytes=1 << 30):
+        pos = pos if pos is not None else _pos(*([10] * B))
+        return lib.gqa_attn_decode_fp8(ctypes.byref(L) if L is not None else
+                                       None, q, pos, B, out, ws, ws_bytes,
+                                       None)
+    L = _layer8()
+    assert call(None) == E_ARG
+    assert call(L, q=None) == E_ARG
+    assert call(L, out=None) == E_ARG
+    assert call(L, ws=None) == E_ARG
+    assert call(L, B=65, pos=_pos(*([1] * 65))) == E_ARG
+    assert call(_layer8(vs=0)) == E_ARG
+    assert call(_layer8(kind=2)) == E_UNS
+    assert call(L, q=FAKE + 4) == E_ALN
+    assert call(L, ws=FAKE + 16) == E_ALN
+    assert call(L, pos=_pos(4096)) == E_POS
+    assert call(_layer8(kind=ga.LOCAL), pos=_pos(1 << 40)) == E_POS
+    need = ga.workspace_bytes(ga.OP_DECODE, ga.GLOBAL, 1, 1, 4096)
+    assert call(L, pos=_pos(4095), ws_bytes=need - 1) == E_WS
