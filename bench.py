@@ -212,6 +212,84 @@ def time_global_decode(ga, torch, layers, qs, outs, ws, positions, kinds,
     return sum(per) / len(per), median(per)
 
 
+FP8_TOKEN_BYTES = 2 * 128 * 2 + 2 * 2 * 4  # codes + scales, K and V
+
+
+def bench_decode_fp8(ga, torch, layers, qs, outs, ws, positions, kinds,
+                     steps, warmup, kernel_reps):
+    """The 52-layer decode step over fp8 caches (E4M3 codes plus one fp32
+    scale per token and KV head): the bf16 caches of the bf16 step are
+    quantised once by the library's fp8 append; a step appends each layer's
+    new token (quantising it) and attends.  Also the global-layer fp8 call
+    alone (split + merge kernels), timed like the roofline kernel.  Bytes
+    counted: 528 per visible token per layer (codes and scales)."""
+    B = len(positions)
+    pos = positions[0]
+    dev = layers[0].k.device
+    l8 = []
+    for l, kind in enumerate(kinds):
+        cap = layers[l].capacity
+        lay = ga.LayerFp8.allocate(kind, B, cap, device=dev)
+        ga.kv_append_fp8(lay, layers[l].k, layers[l].v, [0] * B)
+        l8.append(lay)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6006)
+    kn = [torch.randn((B, 1, ga.HKV, ga.D), generator=gen, device=dev)
+          .to(torch.bfloat16) for _ in kinds]
+    vn = [torch.randn((B, 1, ga.HKV, ga.D), generator=gen, device=dev)
+          .to(torch.bfloat16) for _ in kinds]
+    out8 = [torch.empty_like(o) for o in outs]
+
+    def step():
+        for l in range(N_LAYERS):
+            ga.kv_append_fp8(l8[l], kn[l], vn[l], positions)
+            ga.attn_decode_fp8(l8[l], qs[l], positions, out8[l], ws)
+
+    ms, _, _ = time_graph(torch, step, steps, warmup)
+    # the fp8 step's outputs against the bf16 step's on the same tokens:
+    # only the quantisation of K and V differs
+    for l in (kinds.index(ga.LOCAL), kinds.index(ga.GLOBAL)):
+        ref = torch.empty_like(outs[l])
+        ga.kv_append(layers[l], kn[l], vn[l], positions)
+        ga.attn_decode(layers[l], qs[l], positions, ref)
+        torch.cuda.synchronize()
+        diff = (ref - out8[l]).abs().max().item()
+        if not diff < 0.05:
+            raise RuntimeError("fp8 decode of layer %d differs from bf16 by "
+                               "%g" % (l, diff))
+    glob = [l for l, k in enumerate(kinds) if k == ga.GLOBAL]
+    for l in glob:
+        ga.attn_decode_fp8(l8[l], qs[l], positions, out8[l], ws)
+    torch.cuda.synchronize()
+    calls = [l for _ in range(kernel_reps) for l in glob]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+    ev[0].record()
+    for i, l in enumerate(calls):
+        ga.attn_decode_fp8(l8[l], qs[l], positions, out8[l], ws)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(calls))]
+    kms = sum(per) / len(per)
+    step_bytes = kv_bytes_step(kinds, positions) // 1024 * FP8_TOKEN_BYTES
+    call_bytes = B * (pos + 1) * FP8_TOKEN_BYTES
+    del l8
+    return {"ms_per_step": round(ms, 4),
+            "kv_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              4),
+            "global_call_ms": round(kms, 5),
+            "global_call_median_ms": round(median(per), 5),
+            "global_call_GBps": round(call_bytes / (kms * 1e-3) / 1e9, 2),
+            "global_call_hbm_frac": round(call_bytes / (kms * 1e-3) / 1e9 /
+                                          HBM_PEAK_GBS, 4),
+            "bytes_per_token_layer": FP8_TOKEN_BYTES,
+            "workload": "52-layer decode step over fp8 caches (E4M3 + one "
+                        "fp32 scale per token and KV head), context 131072, "
+                        "batch %d: fp8 append + attend per layer, HIP graph"
+                        % B}
+
+
 def pairs_block(kind, pos0, n, window=2048):
     """Unmasked (query, key) pairs of a block of n tokens at pos0."""
     total = 0
@@ -434,6 +512,9 @@ def main():
                     help="run only the global-layer decode call this many "
                          "times over each of the 13 global layers and print "
                          "its average (for hardware-counter runs)")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="after the bf16 decode step, run only the fp8 "
+                         "decode measurement (skip verify and prefill)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB, "
                          "to scale hardware byte counters")
@@ -527,7 +608,14 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(ga, torch, layers, qs, outs,
                                             positions, kinds)
-    if not args.no_extras:
+    if not args.no_extras or args.fp8_only:
+        line["decode_fp8"] = bench_decode_fp8(
+            ga, torch, layers, qs, outs, ws, positions, kinds, args.steps,
+            args.warmup, args.kernel_reps)
+        line["decode_fp8"]["global_call_vs_bf16"] = round(
+            kms / line["decode_fp8"]["global_call_ms"], 3)
+        print("# fp8 decode done", file=sys.stderr, flush=True)
+    if not args.no_extras and not args.fp8_only:
         line["verify"] = bench_verify(ga, torch, layers, kinds, 1)
         print("# verify done", file=sys.stderr, flush=True)
         line["draft_block"] = bench_draft(ga, torch, layers, kinds, 1)
