@@ -43,7 +43,7 @@ def _ensure_built():
 def measured_traffic(B):
     """HBM bytes per launch of the global-layer decode kernel from the
     committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by a plain copy
-    (profiles/decode_global_131072_b4_hbm_counters.md).  None when the
+    (profiles/decode_131072_hbm_counters.md).  None when the
     counters were taken on other kernel sources or another batch size."""
     import hashlib
     try:
