@@ -141,6 +141,17 @@ __global__ __launch_bounds__(64) void rope_keys_kernel(const BlockParams p) {
   d32[c + 32] = y;
 }
 
+// Largest of 16 scores as a tree of three-input maxima (depth 3, where a
+// running maximum would chain 16 dependent instructions).
+__device__ __forceinline__ float max16(const f32x16_t& v) {
+  float m[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i)
+    m[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+  return fmaxf(fmaxf(fmaxf(m[0], m[1]), m[2]),
+               fmaxf(fmaxf(m[3], m[4]), v[15]));
+}
+
 // Tile t goes to ring slot t % 4, loaded three tiles ahead (direct-to-LDS,
 // so tile t + 3 is in flight while tile t is consumed).  K chunk c of row r
 // sits at chunk
@@ -457,12 +468,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
           S[be][i] = ok ? S[be][i] : -INFINITY;
         }
     }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int be = 0; be < 2; ++be)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, S[be][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) + mb;  // tile max, log2 units
+    float mt = fmaxf(max16(S[0]), max16(S[1]));
+    mt = xmax<32>(mt) + mb;  // tile max, log2 units
     if (__any(mt > m_run + kTauB)) {
       const float mn = fmaxf(m_run, mt);
       const float alpha = mn == m_run ? 1.0f : fast_exp2(m_run - mn);
@@ -595,7 +602,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
   }
 
   // ---- epilogue: this lane holds row `row`, dims 32d + 8(i>>2) + 4 hi5 + i&3
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = xsum<32>(l_run);
   if constexpr (SPLIT) {
     const int prow = (2 * w + (row >> 4)) * kGroup + (row & 15);
     float* base = p.part +
@@ -704,12 +711,9 @@ __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
     }
   }
   // the 8 split lanes of a wave that share a column are 8 apart
+  L = stride8_sum(L);
 #pragma unroll
-  for (int o = 8; o <= 32; o <<= 1) {
-    L += __shfl_xor(L, o, 64);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) O[j] += __shfl_xor(O[j], o, 64);
-  }
+  for (int j = 0; j < 16; ++j) O[j] = stride8_sum(O[j]);
   if ((tid & 63) < 8) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) wsum[w][c][j] = O[j];

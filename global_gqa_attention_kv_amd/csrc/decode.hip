@@ -129,18 +129,6 @@ __device__ __forceinline__ uint32_t cvt_fp8x2_bf16(uint32_t w) {
       uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// Maximum and sum over the 16 lanes of a DPP row.
-__device__ __forceinline__ float row_max(float x) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 16));
-  return x;
-}
-__device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) x += __shfl_xor(x, o, 16);
-  return x;
-}
-
 // s_waitcnt vmcnt(N): at most N of this wave's vector memory operations
 // (here: ring loads) still outstanding.
 template <int N>
@@ -802,10 +790,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
 #pragma unroll
   for (int hl = 0; hl < HW; ++hl) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[hl][e] += __shfl_xor(o[hl][e], 16, 64);
-      o[hl][e] += __shfl_xor(o[hl][e], 32, 64);
-    }
+    for (int e = 0; e < 8; ++e) o[hl][e] = rows_sum(o[hl][e]);
     lsum[hl] = wave_sum(lsum[hl]);
   }
   if (kg == 0) {
@@ -886,14 +871,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
   // sum over the 32 split lanes: the 8 lanes of a wave that share a column
   // are 8 apart, then the four waves
-#pragma unroll
-  for (int o = 8; o <= 32; o <<= 1) {
-    L += __shfl_xor(L, o, 64);
-    O.x += __shfl_xor(O.x, o, 64);
-    O.y += __shfl_xor(O.y, o, 64);
-    O.z += __shfl_xor(O.z, o, 64);
-    O.w += __shfl_xor(O.w, o, 64);
-  }
+  L = stride8_sum(L);
+  O.x = stride8_sum(O.x);
+  O.y = stride8_sum(O.y);
+  O.z = stride8_sum(O.z);
+  O.w = stride8_sum(O.w);
   if ((tid & 63) < 8) {
     wsum[w][c4] = O;
     wl[w][c4] = L;

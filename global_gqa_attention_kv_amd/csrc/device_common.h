@@ -152,15 +152,71 @@ __device__ __forceinline__ void rope_pair(uint32_t& lo, uint32_t& hi,
   hi = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
 }
 
+// Cross-lane reductions with no LDS round trip (a ds_bpermute costs an LDS
+// latency per step): DPP moves inside each 16-lane row -- quad swaps, the
+// half-row mirror (lane i <-> 7 - i of each 8), the row mirror (i <-> 15 - i)
+// and the rotation by 8 (i <-> i ^ 8) -- and gfx950's v_permlane16_swap /
+// v_permlane32_swap across rows, which hand both lanes of a pair (l, l ^ 16
+// or l, l ^ 32) the pair's two values in the same order.  Each step combines
+// two lanes of equal coverage with a commutative operation, so every lane
+// of the reduced group ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                      0xF, false));
+}
+// The swaps are written in assembly: this compiler's builtins for them hand
+// back one of the two results twice when both are combined (an add of the
+// pair came out as one register added to itself).  Two wait states separate
+// the last VALU write of an operand from the swap.
+// every lane l gets the values of lanes l & ~16 and l | 16
+__device__ __forceinline__ void xchg16(uint32_t& lo, uint32_t& hi) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+}
+// every lane l gets the values of lanes l & ~32 and l | 32
+__device__ __forceinline__ void xchg32(uint32_t& lo, uint32_t& hi) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+}
+template <int STRIDE>
+__device__ __forceinline__ float xmax(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  if constexpr (STRIDE == 16) xchg16(a, b); else xchg32(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+template <int STRIDE>
+__device__ __forceinline__ float xsum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  if constexpr (STRIDE == 16) xchg16(a, b); else xchg32(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+// over the 16 lanes of each row
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  return x + dpp_mov<0x140>(x);
+}
+// over lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float rows_sum(float x) {
+  return xsum<32>(xsum<16>(x));
+}
+// over lanes l, l ^ 8, l ^ 16, ..., l ^ 56 (same l % 8)
+__device__ __forceinline__ float stride8_sum(float x) {
+  return rows_sum(x + dpp_mov<0x128>(x));  // row_ror:8
+}
+// over the 64 lanes
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  return xmax<32>(xmax<16>(row_max(x)));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  return rows_sum(row_sum(x));
 }
 
 }  // namespace gqa

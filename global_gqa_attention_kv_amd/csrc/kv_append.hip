@@ -7,6 +7,7 @@
 // wants the sliding-window saving.  One token of one cache is 2 heads x 128
 // bf16 = 512 B; a wave copies K (lanes 0-31) and V (lanes 32-63) of one token
 // with 16-byte loads and stores.
+#include "device_common.h"
 #include "internal.h"
 
 namespace gqa {
@@ -64,8 +65,7 @@ __global__ __launch_bounds__(64) void kv_append_fp8_kernel(
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  amax = row_max(amax);
   const float scale = __fdiv_rn(amax, 448.0f);
   uint32_t c0 = 0, c1 = 0;
   if (amax > 0.0f) {
