@@ -744,6 +744,90 @@ __global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
   }
 }
 
+// The same merge for at most kWaveMergeSplitsB splits, with no LDS and no
+// barrier: one wave per (sequence, token, head), lane 8 sl + c.  Split
+// lane sl takes splits sl, sl + 8, ..., column c dimensions 16c .. 16c + 15;
+// the maximum and the sums are reduced over the eight split lanes of a
+// column (lanes c, c + 8, ..., c + 56) in registers.
+constexpr int kWaveMergeSplitsB = 128;
+template <bool OUT_F32>
+__global__ __launch_bounds__(64) void block_merge_wave_kernel(
+    const BlockParams p) {
+  constexpr int ROWS = kBlkQpw * kGroup;
+  int rest = blockIdx.x;
+  const int h = rest % kHq;
+  rest /= kHq;
+  const int qi = rest % p.n;
+  const int b = rest / p.n;
+  const int g = h / kGroup;
+  const int qg = qi / kBlkQpw;
+  const int prow = (qi - qg * kBlkQpw) * kGroup + (h % kGroup);
+  const float* base =
+      p.part + (((size_t)(b * kHkv + g) * p.qgroups + qg) * p.splits * ROWS +
+                prow) * kPartRow;
+  constexpr size_t sstride = (size_t)ROWS * kPartRow;
+  const int lane = threadIdx.x;
+  const int c = lane & 7, sl = lane >> 3;
+  constexpr int kPer = kWaveMergeSplitsB / 8;
+  float ms[kPer], ls[kPer];
+  uint4 os[kPer][2];  // dims 16c .. 16c + 15 as bf16
+  const int nper = (p.splits + 7) / 8;  // batches holding a split
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    ms[i] = -INFINITY;
+    ls[i] = 0.0f;
+    os[i][0] = os[i][1] = make_uint4(0, 0, 0, 0);
+    if (i >= nper) continue;
+    const int s = sl + 8 * i;
+    const float* ps = base + (size_t)min(s, p.splits - 1) * sstride;
+    ms[i] = s < p.splits ? ps[kD / 2] : -INFINITY;
+    ls[i] = ps[kD / 2 + 1];
+    os[i][0] = *reinterpret_cast<const uint4*>(ps + 8 * c);
+    os[i][1] = *reinterpret_cast<const uint4*>(ps + 8 * c + 4);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) M = fmaxf(M, ms[i]);
+  M = fmaxf(M, dpp_mov<0x128>(M));  // row_ror:8, the other split lane of the row
+  M = xmax<32>(xmax<16>(M));
+  // splits without visible keys (m = -inf) and padding lanes weigh 0
+  float L = 0.0f, O[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) O[j] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const float cw = fast_exp2(ms[i] - M) * ls[i];
+    L += cw;
+    const uint32_t* wv = reinterpret_cast<const uint32_t*>(&os[i][0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      O[2 * j] += bf16_lo(wv[j]) * cw;
+      O[2 * j + 1] += bf16_hi(wv[j]) * cw;
+    }
+  }
+  L = stride8_sum(L);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) O[j] = stride8_sum(O[j]);
+  if (sl != 0) return;
+  const float inv = 1.0f / L;
+  const size_t o = (((size_t)b * p.n + qi) * kHq + h) * kD + 16 * c;
+  if constexpr (OUT_F32) {
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + o);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dst[j] = make_float4(O[4 * j] * inv, O[4 * j + 1] * inv,
+                           O[4 * j + 2] * inv, O[4 * j + 3] * inv);
+  } else {
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + o);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dst[j] = make_uint4(pack_bf16(O[8 * j] * inv, O[8 * j + 1] * inv),
+                          pack_bf16(O[8 * j + 2] * inv, O[8 * j + 3] * inv),
+                          pack_bf16(O[8 * j + 4] * inv, O[8 * j + 5] * inv),
+                          pack_bf16(O[8 * j + 6] * inv, O[8 * j + 7] * inv));
+  }
+}
+
 template <bool LOCAL, bool OUT_F32>
 hipError_t launch_main(const BlockParams& p, const BlockPlan& plan, int B,
                        hipStream_t s) {
@@ -756,8 +840,12 @@ hipError_t launch_main(const BlockParams& p, const BlockPlan& plan, int B,
                        0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((block_merge_kernel<OUT_F32>),
-                       dim3(B * p.n * kHq), dim3(256), 0, s, p);
+    if (p.splits <= kWaveMergeSplitsB)
+      hipLaunchKernelGGL((block_merge_wave_kernel<OUT_F32>),
+                         dim3(B * p.n * kHq), dim3(64), 0, s, p);
+    else
+      hipLaunchKernelGGL((block_merge_kernel<OUT_F32>),
+                         dim3(B * p.n * kHq), dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL((block_attn_kernel<LOCAL, false, OUT_F32>), grid, block,
                        0, s, p);
