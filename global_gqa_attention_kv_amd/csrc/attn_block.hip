@@ -492,6 +492,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
       for (int i = 0; i < 16; ++i) negmb[i] = -nb;
     }
     bf16x8_t P[4];  // 16-key contraction steps: (block be, half tt)
+    // the denominator sums exactly the bf16 weights P.V uses, in four
+    // independent partial sums (a single running sum would chain sixteen
+    // dependent instructions)
+    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int be = 0; be < 2; ++be)
 #pragma unroll
@@ -502,12 +506,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
           const float p0 = fast_exp2(S[be][8 * tt + 2 * j]);
           const float p1 = fast_exp2(S[be][8 * tt + 2 * j + 1]);
           w4[j] = pack_bf16(p0, p1);
-          // the denominator sums exactly the bf16 weights P.V uses
-          l_run = dot2_bf16(w4[j], 0x3F803F80u, l_run);
+          lp[j] = dot2_bf16(w4[j], 0x3F803F80u, lp[j]);
         }
         P[2 * be + tt] = __builtin_bit_cast(
             bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
       }
+    l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
 
     // ---- O^T += V^T P^T over four 16-key steps, four 32-dim blocks; the
     // operands of step c + 1 are read while step c multiplies
