@@ -650,112 +650,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
   }  // work items
 }
 
-// Merge the key splits of one (sequence, token, query head): 32 split lanes
-// x 8 columns of 16 dimensions per workgroup (thread = 8 lane + column), so
-// the split rows are read whole, every split's loads in flight at once.  The
+// Merge the key splits of one (sequence, token, query head), one wave,
+// lane 8 sl + c: split lane sl takes splits sl, sl + 8, ... (every split's
+// loads in flight at once), column c dimensions 16c .. 16c + 15.  The
 // largest split maximum M is found first, so the weighted sums need no
-// rescaling and the split lanes combine by plain addition; with the stored
-// o'_s = o_s / l_s, o = sum 2^(m_s - M) l_s o'_s / sum 2^(m_s - M) l_s.
+// rescaling; with the stored o'_s = o_s / l_s,
+// o = sum 2^(m_s - M) l_s o'_s / sum 2^(m_s - M) l_s.  The maximum and the
+// sums are reduced over the eight split lanes of a column (lanes c, c + 8,
+// ..., c + 56) in registers, with no LDS and no barrier.
+constexpr int kWaveMergeSplitsB = kBlkMaxSplits;
 template <bool OUT_F32>
-__global__ __launch_bounds__(256) void block_merge_kernel(const BlockParams p) {
-  constexpr int ROWS = kBlkQpw * kGroup;
-  int rest = blockIdx.x;
-  const int h = rest % kHq;
-  rest /= kHq;
-  const int qi = rest % p.n;
-  const int b = rest / p.n;
-  const int g = h / kGroup;
-  const int qg = qi / kBlkQpw;
-  const int prow = (qi - qg * kBlkQpw) * kGroup + (h % kGroup);
-  const float* base =
-      p.part + (((size_t)(b * kHkv + g) * p.qgroups + qg) * p.splits * ROWS +
-                prow) * kPartRow;
-  constexpr size_t sstride = (size_t)ROWS * kPartRow;
-  const int tid = threadIdx.x;
-  const int c = tid & 7, sl = tid >> 3, w = tid >> 6;
-  __shared__ float wmax[4];
-  __shared__ float wsum[4][8][17];
-  constexpr int kPer = kMaxSplits / 32;  // the planner keeps splits <= 256
-  float ms[kPer], ls[kPer];
-  uint4 os[kPer][2];  // dims 16c .. 16c + 15 as bf16
-  const int nper = (p.splits + 31) / 32;  // batches holding a split
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    ms[i] = -INFINITY;
-    ls[i] = 0.0f;
-    os[i][0] = os[i][1] = make_uint4(0, 0, 0, 0);
-    if (i >= nper) continue;
-    const int s = sl + 32 * i;
-    const float* ps = base + (size_t)min(s, p.splits - 1) * sstride;
-    ms[i] = s < p.splits ? ps[kD / 2] : -INFINITY;
-    ls[i] = ps[kD / 2 + 1];
-    os[i][0] = *reinterpret_cast<const uint4*>(ps + 8 * c);
-    os[i][1] = *reinterpret_cast<const uint4*>(ps + 8 * c + 4);
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) mx = fmaxf(mx, ms[i]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) wmax[w] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  // splits without visible keys (m = -inf) and padding lanes weigh 0
-  float L = 0.0f, O[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) O[j] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const float cw = fast_exp2(ms[i] - M) * ls[i];
-    L += cw;
-    const uint32_t* wv = reinterpret_cast<const uint32_t*>(&os[i][0]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      O[2 * j] += bf16_lo(wv[j]) * cw;
-      O[2 * j + 1] += bf16_hi(wv[j]) * cw;
-    }
-  }
-  // the 8 split lanes of a wave that share a column are 8 apart
-  L = stride8_sum(L);
-#pragma unroll
-  for (int j = 0; j < 16; ++j) O[j] = stride8_sum(O[j]);
-  if ((tid & 63) < 8) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) wsum[w][c][j] = O[j];
-    wsum[w][c][16] = L;
-  }
-  __syncthreads();
-  if (tid >= 8) return;
-  float r[17];
-#pragma unroll
-  for (int j = 0; j < 17; ++j)
-    r[j] = wsum[0][c][j] + wsum[1][c][j] + wsum[2][c][j] + wsum[3][c][j];
-  const float inv = 1.0f / r[16];
-  const size_t o = (((size_t)b * p.n + qi) * kHq + h) * kD + 16 * c;
-  if constexpr (OUT_F32) {
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + o);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dst[j] = make_float4(r[4 * j] * inv, r[4 * j + 1] * inv,
-                           r[4 * j + 2] * inv, r[4 * j + 3] * inv);
-  } else {
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + o);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      dst[j] = make_uint4(pack_bf16(r[8 * j] * inv, r[8 * j + 1] * inv),
-                          pack_bf16(r[8 * j + 2] * inv, r[8 * j + 3] * inv),
-                          pack_bf16(r[8 * j + 4] * inv, r[8 * j + 5] * inv),
-                          pack_bf16(r[8 * j + 6] * inv, r[8 * j + 7] * inv));
-  }
-}
-
-// The same merge for at most kWaveMergeSplitsB splits, with no LDS and no
-// barrier: one wave per (sequence, token, head), lane 8 sl + c.  Split
-// lane sl takes splits sl, sl + 8, ..., column c dimensions 16c .. 16c + 15;
-// the maximum and the sums are reduced over the eight split lanes of a
-// column (lanes c, c + 8, ..., c + 56) in registers.
-constexpr int kWaveMergeSplitsB = 128;
-template <bool OUT_F32>
-__global__ __launch_bounds__(64) void block_merge_wave_kernel(
+__global__ __launch_bounds__(64) void block_merge_kernel(
     const BlockParams p) {
   constexpr int ROWS = kBlkQpw * kGroup;
   int rest = blockIdx.x;
@@ -844,12 +749,8 @@ hipError_t launch_main(const BlockParams& p, const BlockPlan& plan, int B,
                        0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p.splits <= kWaveMergeSplitsB)
-      hipLaunchKernelGGL((block_merge_wave_kernel<OUT_F32>),
-                         dim3(B * p.n * kHq), dim3(64), 0, s, p);
-    else
-      hipLaunchKernelGGL((block_merge_kernel<OUT_F32>),
-                         dim3(B * p.n * kHq), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((block_merge_kernel<OUT_F32>), dim3(B * p.n * kHq),
+                       dim3(64), 0, s, p);
   } else {
     hipLaunchKernelGGL((block_attn_kernel<LOCAL, false, OUT_F32>), grid, block,
                        0, s, p);
@@ -861,7 +762,7 @@ hipError_t launch_main(const BlockParams& p, const BlockPlan& plan, int B,
 
 hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
                         bool local, bool out_f32, int B, hipStream_t s) {
-  if (plan.qpw != kBlkQpw || p.splits > kMaxSplits || plan.grid < 1 ||
+  if (plan.qpw != kBlkQpw || p.splits > kBlkMaxSplits || plan.grid < 1 ||
       (p.splits > 1 && plan.grid != p.splits * p.qgroups * kHkv * B))
     return hipErrorInvalidValue;
   if (local) {

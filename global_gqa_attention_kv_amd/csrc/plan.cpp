@@ -66,7 +66,7 @@ BlockPlan plan_block(int kind, int B, int n, int64_t max_keys,
   // down to one tile per workgroup (measured on the local verify: one tile
   // per workgroup beat two now that split partials are bf16 rows)
   if (splits > tiles) splits = tiles;
-  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits > kBlkMaxSplits) splits = kBlkMaxSplits;
   if (splits < 1) splits = 1;
   p.splits = (int)splits;
   const int64_t items = splits * groups;

@@ -46,7 +46,7 @@ void shim_plan_block(int kind, int B, int n, long long keys, int cus,
 """
 
 LOCAL, GLOBAL = 0, 1
-TILE, W, MAX_SPLITS = 64, 2048, 256
+TILE, W, MAX_SPLITS, BLK_MAX_SPLITS = 64, 2048, 256, 128
 SHAPES = [(256, 8), (304, 8), (240, 8), (128, 4), (80, 2), (64, 2), (38, 1),
           (32, 1), (8, 1), (1, 1)]
 
@@ -144,7 +144,7 @@ def test_block_plans_cover_and_fit(plans, cus, xcds):
                 groups = p["qgroups"] * 2 * B
                 assert p["qgroups"] == -(-n // 16)
                 wg_keys = W - 1 + 16 if kind == LOCAL else keys
-                assert 1 <= p["splits"] <= min(MAX_SPLITS,
+                assert 1 <= p["splits"] <= min(BLK_MAX_SPLITS,
                                                -(-wg_keys // TILE))
                 items = p["splits"] * groups
                 if p["splits"] > 1:
