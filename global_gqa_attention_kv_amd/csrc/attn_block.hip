@@ -118,10 +118,14 @@ __device__ __forceinline__ int64_t ring_prior(int64_t pos0) {
 
 // Local layers: write the RoPE-rotated keys of positions p0 - W' .. p0+n-1
 // (W' = min(p0, 2048) cached positions before the block) into k_lin, rotated
-// by their offset from p0.  One wave per key row (2 heads x 128 dims).
-__global__ __launch_bounds__(64) void rope_keys_kernel(const BlockParams p) {
+// by their offset from p0.  16 lanes per key row: lane c takes dimensions
+// 4c .. 4c + 3 against 64 + 4c .. of both KV heads, so each angle's sine and
+// cosine serve both heads; 16 rows per 256-thread workgroup.
+constexpr int kRopeRowsPerWG = 16;
+__global__ __launch_bounds__(256) void rope_keys_kernel(const BlockParams p) {
   const int b = blockIdx.y;
-  const int r = blockIdx.x;
+  const int r = blockIdx.x * kRopeRowsPerWG + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
   const int64_t pos0 = p.pos0[b];
   const int64_t wprior = ring_prior(pos0);
   if (r >= wprior + p.n) return;
@@ -130,15 +134,36 @@ __global__ __launch_bounds__(64) void rope_keys_kernel(const BlockParams p) {
       j < pos0 ? p.k_cache + (int64_t)b * p.seq_stride +
                      (j & (kW - 1)) * kTokenElems
                : p.k_blk + ((int64_t)b * p.n + (j - pos0)) * kTokenElems;
-  const int lane = threadIdx.x;
-  const int head = lane >> 5, c = lane & 31;  // dims 2c, 2c+1 and +64
-  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src + head * kD);
-  uint32_t x = s32[c], y = s32[c + 32];
-  rope_pair(x, y, (float)(j - pos0), p.rope_rev[2 * c], p.rope_rev[2 * c + 1]);
-  uint32_t* d32 = reinterpret_cast<uint32_t*>(
-      p.k_lin + ((int64_t)b * p.klin_rows + r) * kTokenElems + head * kD);
-  d32[c] = x;
-  d32[c + 32] = y;
+  uint16_t* dst = p.k_lin + ((int64_t)b * p.klin_rows + r) * kTokenElems;
+  const float delta = (float)(j - pos0);
+  // angles of frequencies 4c .. 4c + 3 (dims 4c + i pair with 64 + 4c + i)
+  float sn[4], cs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float t = delta * p.rope_rev[4 * c + i];
+    t -= rintf(t);
+    sincos_rev(t, &sn[i], &cs[i]);
+  }
+#pragma unroll
+  for (int h = 0; h < kHkv; ++h) {
+    const uint2 xw = *reinterpret_cast<const uint2*>(src + h * kD + 4 * c);
+    const uint2 yw =
+        *reinterpret_cast<const uint2*>(src + h * kD + kD / 2 + 4 * c);
+    const float x[4] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y),
+                        bf16_hi(xw.y)};
+    const float y[4] = {bf16_lo(yw.x), bf16_hi(yw.x), bf16_lo(yw.y),
+                        bf16_hi(yw.y)};
+    float a[4], e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = x[i] * cs[i] - y[i] * sn[i];
+      e[i] = y[i] * cs[i] + x[i] * sn[i];
+    }
+    *reinterpret_cast<uint2*>(dst + h * kD + 4 * c) =
+        make_uint2(pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]));
+    *reinterpret_cast<uint2*>(dst + h * kD + kD / 2 + 4 * c) =
+        make_uint2(pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]));
+  }
 }
 
 // Largest of 16 scores as a tree of three-input maxima (depth 3, where a
@@ -767,8 +792,11 @@ hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
     return hipErrorInvalidValue;
   if (local) {
     if (p.splits == 1) {  // keys rotated once into the workspace
-      hipLaunchKernelGGL(rope_keys_kernel, dim3((unsigned)p.klin_rows, B),
-                         dim3(64), 0, s, p);
+      hipLaunchKernelGGL(rope_keys_kernel,
+                         dim3((unsigned)((p.klin_rows + kRopeRowsPerWG - 1) /
+                                         kRopeRowsPerWG),
+                              B),
+                         dim3(256), 0, s, p);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

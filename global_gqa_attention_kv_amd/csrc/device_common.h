@@ -134,24 +134,6 @@ __device__ __forceinline__ void sincos_rev(float r, float* s, float* c) {
   *c = __builtin_amdgcn_cosf(r);
 }
 
-// RoPE on bf16 data: rotate the pairs (lo[i], hi[i]) -- dims d and d + 64
-// of one head -- by `delta` positions, where rev[i] is the pair's frequency
-// in revolutions per position.  The angle is reduced to [-1/2, 1/2]
-// revolution before the hardware sine/cosine; results are rounded to bf16.
-__device__ __forceinline__ void rope_pair(uint32_t& lo, uint32_t& hi,
-                                          float delta, float f0, float f1) {
-  const float x0 = bf16_lo(lo), x1 = bf16_hi(lo);
-  const float y0 = bf16_lo(hi), y1 = bf16_hi(hi);
-  float r0 = delta * f0, r1 = delta * f1;
-  r0 -= rintf(r0);
-  r1 -= rintf(r1);
-  float s0, c0, s1, c1;
-  sincos_rev(r0, &s0, &c0);
-  sincos_rev(r1, &s1, &c1);
-  lo = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
-  hi = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
-}
-
 // Cross-lane reductions with no LDS round trip (a ds_bpermute costs an LDS
 // latency per step): DPP moves inside each 16-lane row -- quad swaps, the
 // half-row mirror (lane i <-> 7 - i of each 8), the row mirror (i <-> 15 - i)
