@@ -192,6 +192,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
     const int r = blockIdx.x % (X * HG);
     unit = (blockIdx.x / (X * HG)) * X + r % X;
     hg = r / X;
+  } else {
+    // When the (sequence, KV head) pairs divide evenly over the XCDs, all
+    // splits of one pair run on one XCD (ids X apart), where the merge
+    // kernel's workgroups for that pair run too, reading the partials from
+    // that XCD's L2.
+    const int X = p.xcds, S = p.splits, BG = p.units / S;
+    if (X > 1 && BG % X == 0) {
+      const int xcd = blockIdx.x % X, s = blockIdx.x / X;
+      unit = (xcd + X * (s / S)) * S + s % S;
+    }
   }
   if (unit >= p.units) return;  // padding of the XCD-aware grid
   const int split = unit % p.splits;
@@ -819,9 +829,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_split_kernel(
 // need no rescaling and the split lanes combine by plain addition.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const DecodeParams p, int hpw) {
-  const int dq = blockIdx.x & 3;
-  const int h = (blockIdx.x >> 2) % kHq;
-  const int b = (blockIdx.x >> 2) / kHq;
+  int dq = blockIdx.x & 3;
+  int h = (blockIdx.x >> 2) % kHq;
+  int b = (blockIdx.x >> 2) / kHq;
+  {
+    // the split kernel's XCD grouping (one (sequence, KV head) pair per
+    // XCD): this workgroup's pair is the one whose splits ran on its XCD
+    const int X = p.xcds, BG = (int)gridDim.x / (kGroup * 4);
+    if (hpw == kGroup && X > 1 && BG % X == 0) {
+      const int xcd = blockIdx.x % X, s = blockIdx.x / X;
+      const int bg = xcd + X * (s / (kGroup * 4)), r = s % (kGroup * 4);
+      b = bg / kHkv;
+      h = (bg % kHkv) * kGroup + r / 4;
+      dq = r % 4;
+    }
+  }
   const int g = h / kGroup, hh = h % kGroup;
   const int hg = hh / hpw, hl = hh % hpw;  // head group, head within it
   const int pf = hpw * (kD + 2);
