@@ -12,7 +12,6 @@ PyTorch provides device memory and streams only.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch

@@ -18,7 +18,7 @@ import torch
 import global_gqa_attention_kv_amd as ga
 import oracle
 import synth_inputs as si
-from tests._util import check_close, fill_layer, oracle_decode, sentinel_cache
+from tests._util import check_close, fill_layer, sentinel_cache
 
 pytestmark = pytest.mark.gpu
 

@@ -20,7 +20,6 @@ import pytest
 import torch
 
 import global_gqa_attention_kv_amd as ga
-import oracle
 import synth_inputs as si
 from oracle import fp8
 from tests._util import check_close

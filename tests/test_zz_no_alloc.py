@@ -9,7 +9,6 @@ fp64 oracle within the tolerance, and leave the same cache bytes.  The
 scratch keeps the previous call's partials, so the smaller second call also
 shows that nothing of the first leaks into it.  A graph capture of the call
 (no allocation inside) replays to the same result."""
-import numpy as np
 import pytest
 import torch
 
