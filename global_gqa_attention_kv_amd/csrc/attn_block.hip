@@ -42,7 +42,10 @@
 //  * Verification splits each sequence's key range across workgroups (down
 //    to one tile each) and merges the partial rows in a second kernel; a
 //    partial row is the split's output divided by its own denominator, as
-//    bf16, plus the maximum and the denominator in fp32.
+//    fp16 scaled by a power of two that puts the row's largest magnitude in
+//    [2^14, 2^15), plus the maximum, the denominator and the inverse scale in
+//    fp32 (fp16's 11-bit significand keeps this intermediate rounding an
+//    eighth of a bf16 rounding at the same 2 bytes per element).
 #include <type_traits>
 
 #include "device_common.h"
@@ -62,9 +65,26 @@ constexpr int kSlotB = 2 * kTileB;          // K tile, then V tile
 constexpr int kRing = 4;                    // tile slots in LDS (128 KB)
 constexpr int kWaves = kBlkQpw / 2;         // 8 waves of 32 rows
 // Partial row of a key split, in 4-byte words: words 0..63 the row's output
-// over the split normalised by its own denominator (o / l) as 128 bf16,
-// word 64 the maximum m, word 65 the denominator l (fp32), 2 words padding.
+// over the split normalised by its own denominator, times 2^(15 - e) where
+// 2^(e - 1) <= max |o / l| < 2^e, as 128 fp16; word 64 the maximum m, word
+// 65 the denominator l, word 66 the inverse scale 2^(e - 15) (fp32), word 67
+// padding.
 constexpr int kPartRow = 68;
+// the exponent e is clamped so both scales stay normal fp32 numbers (rows
+// below 2^-100 keep their absolute error far under any bf16 rounding)
+constexpr int kPartExpMin = -100;
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  f16x2_t r = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
@@ -639,19 +659,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
                     split) * ROWS + prow) * kPartRow;
     // a row with no visible key in this split (l = 0) stores zeros
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    // the row's largest |o| (64 dimensions here, 64 in the lane 32 away)
+    float amax = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(O[d][i]));
+    int e;
+    (void)frexpf(xmax<32>(amax) * inv, &e);
+    e = max(e, kPartExpMin);
+    const float sc = inv * ldexpf(1.0f, 15 - e);
     uint32_t* ob = reinterpret_cast<uint32_t*>(base);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
         *reinterpret_cast<uint2*>(ob + (32 * d + 8 * ib + 4 * hi5) / 2) =
-            make_uint2(pack_bf16(O[d][4 * ib] * inv, O[d][4 * ib + 1] * inv),
-                       pack_bf16(O[d][4 * ib + 2] * inv,
-                                 O[d][4 * ib + 3] * inv));
-    if (hi5 == 0) {
-      base[kD / 2] = m_run;
-      base[kD / 2 + 1] = l_tot;
-    }
+            make_uint2(pack_f16(O[d][4 * ib] * sc, O[d][4 * ib + 1] * sc),
+                       pack_f16(O[d][4 * ib + 2] * sc,
+                                O[d][4 * ib + 3] * sc));
+    if (hi5 == 0)
+      *reinterpret_cast<float4*>(base + kD / 2) =
+          make_float4(m_run, l_tot, ldexpf(1.0f, e - 15), 0.0f);
   } else if (row_valid) {
     const float inv = 1.0f / l_tot;
     const size_t obase = (((size_t)b * p.n + qi) * kHq + head) * kD;
@@ -679,7 +708,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
 // lane 8 sl + c: split lane sl takes splits sl, sl + 8, ... (every split's
 // loads in flight at once), column c dimensions 16c .. 16c + 15.  The
 // largest split maximum M is found first, so the weighted sums need no
-// rescaling; with the stored o'_s = o_s / l_s,
+// rescaling; with the stored o'_s = o_s / l_s (held as o'_s / r_s in fp16,
+// r_s the row's inverse scale),
 // o = sum 2^(m_s - M) l_s o'_s / sum 2^(m_s - M) l_s.  The maximum and the
 // sums are reduced over the eight split lanes of a column (lanes c, c + 8,
 // ..., c + 56) in registers, with no LDS and no barrier.
@@ -703,25 +733,29 @@ __global__ __launch_bounds__(64) void block_merge_kernel(
   const int lane = threadIdx.x;
   const int c = lane & 7, sl = lane >> 3;
   constexpr int kPer = kWaveMergeSplitsB / 8;
-  float ms[kPer], ls[kPer];
-  uint4 os[kPer][2];  // dims 16c .. 16c + 15 as bf16
+  float4 st[kPer];    // m, l, inverse scale
+  uint4 os[kPer][2];  // dims 16c .. 16c + 15 as scaled fp16
   const int nper = (p.splits + 7) / 8;  // batches holding a split
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    ms[i] = -INFINITY;
-    ls[i] = 0.0f;
+    st[i] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
     os[i][0] = os[i][1] = make_uint4(0, 0, 0, 0);
     if (i >= nper) continue;
-    const int s = sl + 8 * i;
-    const float* ps = base + (size_t)min(s, p.splits - 1) * sstride;
-    ms[i] = s < p.splits ? ps[kD / 2] : -INFINITY;
-    ls[i] = ps[kD / 2 + 1];
+    const float* ps =
+        base + (size_t)min(sl + 8 * i, p.splits - 1) * sstride;
+    st[i] = *reinterpret_cast<const float4*>(ps + kD / 2);
     os[i][0] = *reinterpret_cast<const uint4*>(ps + 8 * c);
     os[i][1] = *reinterpret_cast<const uint4*>(ps + 8 * c + 4);
   }
+  // lanes past the last split (they loaded the last split again) weigh 0;
+  // masked only now, so no batch's loads wait for an earlier batch's
+  float ms[kPer];
   float M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) M = fmaxf(M, ms[i]);
+  for (int i = 0; i < kPer; ++i) {
+    ms[i] = sl + 8 * i < p.splits ? st[i].x : -INFINITY;
+    M = fmaxf(M, ms[i]);
+  }
   M = fmaxf(M, dpp_mov<0x128>(M));  // row_ror:8, the other split lane of the row
   M = xmax<32>(xmax<16>(M));
   // splits without visible keys (m = -inf) and padding lanes weigh 0
@@ -730,13 +764,14 @@ __global__ __launch_bounds__(64) void block_merge_kernel(
   for (int j = 0; j < 16; ++j) O[j] = 0.0f;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const float cw = fast_exp2(ms[i] - M) * ls[i];
+    const float cw = fast_exp2(ms[i] - M) * st[i].y;
     L += cw;
+    const float cwr = cw * st[i].z;
     const uint32_t* wv = reinterpret_cast<const uint32_t*>(&os[i][0]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      O[2 * j] += bf16_lo(wv[j]) * cw;
-      O[2 * j + 1] += bf16_hi(wv[j]) * cw;
+      O[2 * j] += f16_lo(wv[j]) * cwr;
+      O[2 * j + 1] += f16_hi(wv[j]) * cwr;
     }
   }
   L = stride8_sum(L);

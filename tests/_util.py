@@ -16,6 +16,22 @@ MEAN_ABS = 2e-3
 # tenth of the output's RMS.
 LONG_CONTEXT = 32768
 MAX_REL_LONG = 0.1
+# Two library paths that compute the same rows with bf16 outputs (a chunked
+# prefill and a whole one) round at different points, so their outputs may
+# sit on neighbouring bf16 values: one bf16 step is 2^-6 = 0.0156 for
+# magnitudes in [2, 4).  Such comparisons allow the larger of SAME_ABS and
+# one bf16 step at the element's magnitude.
+SAME_ABS = 1e-2
+
+
+def same_path_excess(a, b):
+    """Largest amount by which |a - b| exceeds max(SAME_ABS, one bf16 step
+    at max(|a|, |b|)), elementwise (<= 0 when the two outputs agree)."""
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    mag = np.maximum(np.abs(a), np.abs(b))
+    step = np.spacing(mag) * np.float32(2 ** 16)  # bf16 keeps 8 of fp32's 24 bits
+    return float((np.abs(a - b) - np.maximum(SAME_ABS, step)).max())
 
 
 def sentinel_cache(kind, B, capacity=None, device="cuda"):

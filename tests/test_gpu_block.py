@@ -18,7 +18,8 @@ import torch
 import global_gqa_attention_kv_amd as ga
 import oracle
 import synth_inputs as si
-from tests._util import check_close, fill_layer, sentinel_cache
+from tests._util import (check_close, fill_layer, same_path_excess,
+                         sentinel_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -202,7 +203,8 @@ def test_prefill_then_append_chunks_match_single_chunk():
     torch.cuda.synchronize()
     both = torch.cat([first, second], dim=1)
     diff = (both.float() - whole.float()).abs().max().item()
-    assert diff <= 1e-2, diff
+    assert same_path_excess(both.float().cpu().numpy(),
+                            whole.float().cpu().numpy()) <= 0, diff
 
 
 LAST0 = 131072 - 4096  # first position of the last 4096-token chunk
