@@ -295,6 +295,7 @@ static int block_impl(const gqa_layer* layer, const void* q,
   p.klin_rows = (int64_t)kW + n;
   p.n = n;
   p.qgroups = plan.qgroups;
+  p.qpw = plan.qpw;
   p.splits = plan.splits;
   p.batch = B;
   p.together = together ? 1 : 0;

@@ -23,7 +23,10 @@
 //    16 query heads of one KV head (256 rows, 8 waves of 32 rows = 2 tokens
 //    x 16 heads), so every K/V tile staged in LDS serves 256 rows (GQA
 //    reuse).  8 waves (two per SIMD) and 224 VGPRs each: one workgroup per
-//    CU.
+//    CU.  Local layers with key splits (verification) take 8 tokens per
+//    workgroup (4 waves, 128 rows): there each workgroup holds one or two
+//    tiles and its chain of loads and products is latency, which half the
+//    rows shorten.
 //  * Scores are formed transposed, S^T = K Q^T, so each lane ends up owning
 //    one row and 16 keys of every 32-key block: the row maximum is 31 in-lane
 //    max operations plus one exchange with the partner lane 32 away, and the
@@ -63,7 +66,6 @@ constexpr float kTauB = 8.0f;
 constexpr int kTileB = kBlkTile * 256;      // one 64-key tile of K or V
 constexpr int kSlotB = 2 * kTileB;          // K tile, then V tile
 constexpr int kRing = 4;                    // tile slots in LDS (128 KB)
-constexpr int kWaves = kBlkQpw / 2;         // 8 waves of 32 rows
 // Partial row of a key split, in 4-byte words: words 0..63 the row's output
 // over the split normalised by its own denominator, times 2^(15 - e) where
 // 2^(e - 1) <= max |o / l| < 2^e, as 128 fp16; word 64 the maximum m, word
@@ -204,11 +206,10 @@ __device__ __forceinline__ float max16(const f32x16_t& v) {
 // keys hit distinct banks; V chunk c at slot c ^ X(r & 3), X = {0, 4, 10,
 // 14}: the four keys of a 16-lane group of ds_read_b64_tr_b16, and the 64
 // bytes of each key read by a 32-lane half, land on distinct banks.
-template <bool LOCAL, bool SPLIT, bool OUT_F32>
-__global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
+template <int QPW, bool LOCAL, bool SPLIT, bool OUT_F32>
+__global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
     const BlockParams p) {
-  constexpr int QPW = kBlkQpw;
-  constexpr int WAVES = kWaves;
+  constexpr int WAVES = QPW / 2;  // waves of 32 rows (2 tokens x 16 heads)
   constexpr int RING = kRing;
   constexpr int ROWS = QPW * kGroup;
   constexpr int RPW = kBlkTile / WAVES;   // tile rows each wave loads
@@ -583,41 +584,52 @@ __global__ __launch_bounds__(kWaves * 64, 1) void block_attn_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
 
-  // ROTK: thread i rotates item i of a landed K tile, item u = (key row
-  // u / 8, dims 8 (u % 8) .. + 7 against dims 64 + 8 (u % 8) ..), by the
-  // key's offset from p0 (the queries carry theirs); the sines and cosines
-  // are taken before the tile is waited for, so they overlap its load.
-  static_assert(!ROTK || WAVES * 64 == kBlkTile * 8, "one item per thread");
-  float rc[8], rs[8];
+  // ROTK: thread i rotates items i, i + NT, ... of a landed K tile, item
+  // u = (key row u / 8, dims 8 (u % 8) .. + 7 against dims 64 + 8 (u % 8)
+  // ..), by the key's offset from p0 (the queries carry theirs); the sines
+  // and cosines are taken before the tile is waited for, so they overlap
+  // its load.
+  constexpr int NT = WAVES * 64;
+  constexpr int RIT = kBlkTile * 8 / NT;  // items per thread
+  static_assert(RIT * NT == kBlkTile * 8, "whole items per thread");
+  float rc[RIT][8], rs[RIT][8];
   auto rope_angles = [&](int t) {
     const int kb = k_lo + (t_begin + t) * kBlkTile;
-    const int j = min(kb + (tid >> 3), k_hi - 1);
-    const float delta = (float)(j - pos0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float r = delta * p.rope_rev[(tid & 7) * 8 + e];
-      r -= rintf(r);
-      sincos_rev(r, &rs[e], &rc[e]);
+    for (int it = 0; it < RIT; ++it) {
+      const int u = tid + it * NT;
+      const int j = min(kb + (u >> 3), k_hi - 1);
+      const float delta = (float)(j - pos0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float r = delta * p.rope_rev[(u & 7) * 8 + e];
+        r -= rintf(r);
+        sincos_rev(r, &rs[it][e], &rc[it][e]);
+      }
     }
   };
   auto rope_tile = [&](auto SLOT) {
-    const int r = tid >> 3, cp = tid & 7;
-    lds_u32x4_t* lo = reinterpret_cast<lds_u32x4_t*>(
-        lds_base + SLOT * kSlotB + r * 256 + ((cp ^ (r & 15)) << 4));
-    lds_u32x4_t* hi = reinterpret_cast<lds_u32x4_t*>(
-        lds_base + SLOT * kSlotB + r * 256 + (((cp + 8) ^ (r & 15)) << 4));
-    u32x4_t a = *lo, c = *hi;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x0 = bf16_lo(a[e]), x1 = bf16_hi(a[e]);
-      const float y0 = bf16_lo(c[e]), y1 = bf16_hi(c[e]);
-      const float c0 = rc[2 * e], s0 = rs[2 * e];
-      const float c1 = rc[2 * e + 1], s1 = rs[2 * e + 1];
-      a[e] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
-      c[e] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+    for (int it = 0; it < RIT; ++it) {
+      const int u = tid + it * NT;
+      const int r = u >> 3, cp = u & 7;
+      lds_u32x4_t* lo = reinterpret_cast<lds_u32x4_t*>(
+          lds_base + SLOT * kSlotB + r * 256 + ((cp ^ (r & 15)) << 4));
+      lds_u32x4_t* hi = reinterpret_cast<lds_u32x4_t*>(
+          lds_base + SLOT * kSlotB + r * 256 + (((cp + 8) ^ (r & 15)) << 4));
+      u32x4_t a = *lo, c = *hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = bf16_lo(a[e]), x1 = bf16_hi(a[e]);
+        const float y0 = bf16_lo(c[e]), y1 = bf16_hi(c[e]);
+        const float c0 = rc[it][2 * e], s0 = rs[it][2 * e];
+        const float c1 = rc[it][2 * e + 1], s1 = rs[it][2 * e + 1];
+        a[e] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+        c[e] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+      }
+      *lo = a;
+      *hi = c;
     }
-    *lo = a;
-    *hi = c;
   };
 
   // tile t -> slot t % RING, loaded RING - 1 tiles ahead; the loop is
@@ -717,19 +729,19 @@ constexpr int kWaveMergeSplitsB = kBlkMaxSplits;
 template <bool OUT_F32>
 __global__ __launch_bounds__(64) void block_merge_kernel(
     const BlockParams p) {
-  constexpr int ROWS = kBlkQpw * kGroup;
+  const int ROWS = p.qpw * kGroup;
   int rest = blockIdx.x;
   const int h = rest % kHq;
   rest /= kHq;
   const int qi = rest % p.n;
   const int b = rest / p.n;
   const int g = h / kGroup;
-  const int qg = qi / kBlkQpw;
-  const int prow = (qi - qg * kBlkQpw) * kGroup + (h % kGroup);
+  const int qg = qi / p.qpw;
+  const int prow = (qi - qg * p.qpw) * kGroup + (h % kGroup);
   const float* base =
       p.part + (((size_t)(b * kHkv + g) * p.qgroups + qg) * p.splits * ROWS +
                 prow) * kPartRow;
-  constexpr size_t sstride = (size_t)ROWS * kPartRow;
+  const size_t sstride = (size_t)ROWS * kPartRow;
   const int lane = threadIdx.x;
   const int c = lane & 7, sl = lane >> 3;
   constexpr int kPer = kWaveMergeSplitsB / 8;
@@ -803,17 +815,25 @@ hipError_t launch_main(const BlockParams& p, const BlockPlan& plan, int B,
   // without key splits: at most one workgroup per CU, each walking its
   // items (the kernel derives the walk from the grid)
   const dim3 grid(plan.grid);
-  const dim3 block(kWaves * 64);
   if (p.splits > 1) {
-    hipLaunchKernelGGL((block_attn_kernel<LOCAL, true, OUT_F32>), grid, block,
-                       0, s, p);
+    bool small = false;
+    if constexpr (LOCAL) small = plan.qpw == kBlkQpwSmall;
+    if constexpr (LOCAL) {
+      if (small)
+        hipLaunchKernelGGL(
+            (block_attn_kernel<kBlkQpwSmall, true, true, OUT_F32>), grid,
+            dim3(kBlkQpwSmall * 32), 0, s, p);
+    }
+    if (!small)
+      hipLaunchKernelGGL((block_attn_kernel<kBlkQpw, LOCAL, true, OUT_F32>),
+                         grid, dim3(kBlkQpw * 32), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((block_merge_kernel<OUT_F32>), dim3(B * p.n * kHq),
                        dim3(64), 0, s, p);
   } else {
-    hipLaunchKernelGGL((block_attn_kernel<LOCAL, false, OUT_F32>), grid, block,
-                       0, s, p);
+    hipLaunchKernelGGL((block_attn_kernel<kBlkQpw, LOCAL, false, OUT_F32>),
+                       grid, dim3(kBlkQpw * 32), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -822,7 +842,10 @@ hipError_t launch_main(const BlockParams& p, const BlockPlan& plan, int B,
 
 hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
                         bool local, bool out_f32, int B, hipStream_t s) {
-  if (plan.qpw != kBlkQpw || p.splits > kBlkMaxSplits || plan.grid < 1 ||
+  // 8-token workgroups only for local layers with key splits
+  const bool small = local && p.splits > 1 && plan.qpw == kBlkQpwSmall;
+  if ((plan.qpw != kBlkQpw && !small) || p.qpw != plan.qpw ||
+      p.splits > kBlkMaxSplits || plan.grid < 1 ||
       (p.splits > 1 && plan.grid != p.splits * p.qgroups * kHkv * B))
     return hipErrorInvalidValue;
   if (local) {

@@ -128,6 +128,7 @@ struct BlockParams {
   int32_t splits;
   int32_t batch;            // B
   int32_t together;         // 1: every query sees the whole block (global)
+  int32_t qpw;              // query tokens per workgroup (the plan's)
   float scale_log2;
   float rope_rev[kD / 2];
   int64_t pos0[kMaxBatch];

@@ -49,27 +49,39 @@ size_t decode_ws_bytes(int B, const DecodePlan& plan) {
 // range is split across workgroups (down to one 64-key tile each) only when
 // the query groups alone cannot give every CU a workgroup: always for
 // verification (<= 16 tokens), for short prefills.  Without splits at most
-// one workgroup per CU is launched, each walking several work items.
+// one workgroup per CU is launched, each walking several work items.  Local
+// layers whose keys are split take 8 tokens per workgroup (4 waves) as long
+// as the groups of 8 still leave CUs over: each workgroup then holds one or
+// two tiles, its chain of query load, tile rotation, products and partial
+// rows is latency, and half the rows shorten it.
 BlockPlan plan_block(int kind, int B, int n, int64_t max_keys,
                      const DeviceShape& dev) {
   const int cus = cus_of(dev);
   BlockPlan p;
-  p.qpw = kBlkQpw;
-  p.qgroups = (n + p.qpw - 1) / p.qpw;
-  // keys one workgroup may see: its window (local) or everything before it
-  const int64_t wg_keys =
-      kind == GQA_LOCAL ? (int64_t)kW - 1 + p.qpw : max_keys;
-  const int64_t tiles = (wg_keys + kBlkTile - 1) / kBlkTile;
-  const int64_t groups = (int64_t)p.qgroups * kHkv * B;
-  int64_t splits = 1;
-  if (groups < cus) splits = (cus + groups - 1) / groups;
-  // down to one tile per workgroup (measured on the local verify: one tile
-  // per workgroup beat two now that split partials are bf16 rows)
-  if (splits > tiles) splits = tiles;
-  if (splits > kBlkMaxSplits) splits = kBlkMaxSplits;
-  if (splits < 1) splits = 1;
-  p.splits = (int)splits;
-  const int64_t items = splits * groups;
+  auto shape = [&](int qpw) {
+    p.qpw = qpw;
+    p.qgroups = (n + qpw - 1) / qpw;
+    // keys one workgroup may see: its window (local) or everything before it
+    const int64_t wg_keys =
+        kind == GQA_LOCAL ? (int64_t)kW - 1 + qpw : max_keys;
+    const int64_t tiles = (wg_keys + kBlkTile - 1) / kBlkTile;
+    const int64_t groups = (int64_t)p.qgroups * kHkv * B;
+    int64_t splits = 1;
+    if (groups < cus) splits = (cus + groups - 1) / groups;
+    // down to one tile per workgroup (measured on the local verify: one
+    // tile per workgroup beat two now that split partials are 2-byte rows)
+    if (splits > tiles) splits = tiles;
+    if (splits > kBlkMaxSplits) splits = kBlkMaxSplits;
+    if (splits < 1) splits = 1;
+    p.splits = (int)splits;
+    return groups;
+  };
+  int64_t groups = shape(kBlkQpw);
+  if (kind == GQA_LOCAL && p.splits > 1) {
+    groups = shape(kBlkQpwSmall);
+    if (p.splits == 1) groups = shape(kBlkQpw);  // groups of 8 fill the CUs
+  }
+  const int64_t items = (int64_t)p.splits * groups;
   p.walks = p.splits > 1 ? 1 : (int)((items + cus - 1) / cus);
   p.grid = (int)((items + p.walks - 1) / p.walks);
   // local layers without key splits read pre-rotated keys from the

@@ -61,6 +61,7 @@ size_t decode_ws_bytes(int B, const DecodePlan& plan);
 // ---------------------------------------------------------------- block
 constexpr int kBlkTile = 64;               // keys per tile
 constexpr int kBlkQpw = 16;                // query tokens per workgroup
+constexpr int kBlkQpwSmall = 8;            // local layers with key splits
 constexpr int kBlkMaxSplits = 128;         // key splits of a block call
 
 struct BlockPlan {

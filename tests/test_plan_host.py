@@ -141,16 +141,25 @@ def test_block_plans_cover_and_fit(plans, cus, xcds):
                            (4096, 4096), (4096, 131072)):
                 keys = min(ctx, W) if kind == LOCAL else ctx
                 p = block(kind, B, n, keys, cus, xcds)
+                qpw = p["qpw"]
+                # 8-token groups only for local layers with key splits, and
+                # whenever those still leave CUs over
+                if qpw == 8:
+                    assert kind == LOCAL and p["splits"] > 1
+                else:
+                    assert qpw == 16
+                    if kind == LOCAL and p["splits"] > 1:
+                        assert -(-n // 8) * 2 * B >= cus
                 groups = p["qgroups"] * 2 * B
-                assert p["qgroups"] == -(-n // 16)
-                wg_keys = W - 1 + 16 if kind == LOCAL else keys
+                assert p["qgroups"] == -(-n // qpw)
+                wg_keys = W - 1 + qpw if kind == LOCAL else keys
                 assert 1 <= p["splits"] <= min(BLK_MAX_SPLITS,
                                                -(-wg_keys // TILE))
                 items = p["splits"] * groups
                 if p["splits"] > 1:
                     assert p["grid"] == items and p["walks"] == 1
                     assert groups < cus
-                    assert p["part"] >= groups * p["splits"] * 256 * 272
+                    assert p["part"] >= groups * p["splits"] * qpw * 16 * 272
                 else:
                     assert p["part"] == 0
                     assert p["grid"] <= cus
@@ -164,11 +173,11 @@ def test_block_plans_cover_and_fit(plans, cus, xcds):
 def test_block_plans_on_a_full_mi355x(plans):
     _, block = plans
     # verify at 131056 + 16, batch 1: 256 workgroups of 16 tiles (global),
-    # 33 splits of one tile per KV head (local)
+    # 33 splits of one tile per KV head and 8-token group (local)
     g = block(GLOBAL, 1, 16, 131072, 256)
-    assert (g["splits"], g["grid"]) == (128, 256)
+    assert (g["qpw"], g["splits"], g["grid"]) == (16, 128, 256)
     loc = block(LOCAL, 1, 16, 2048, 256)
-    assert loc["splits"] == 33
+    assert (loc["qpw"], loc["splits"], loc["grid"]) == (8, 33, 132)
     # prefill chunk of 4096: 512 work items walked by 256 workgroups
     pf = block(GLOBAL, 1, 4096, 131072, 256)
     assert (pf["splits"], pf["grid"], pf["walks"]) == (1, 256, 2)
