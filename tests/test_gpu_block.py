@@ -39,11 +39,16 @@ def _oracle_rows(kind, q_cpu, streams, pos0, rows):
     return np.stack(out)
 
 
-def _setup(kind, pos0, n, seed, capacity=None):
+def _setup(kind, pos0, n, seed, capacity=None, v_scale=1.0):
     """Caches holding every position before pos0[b]; returns the layer,
-    the logical streams (positions 0 .. pos0+n-1), the block tensors."""
+    the logical streams (positions 0 .. pos0+n-1), the block tensors.
+    v_scale (a power of two, so the bf16 values scale exactly) multiplies
+    every value vector."""
     B = len(pos0)
     streams = [si.stream(si.seq_seed(seed, b), pos0[b] + n) for b in range(B)]
+    if v_scale != 1.0:
+        streams = [(k, (v.float() * v_scale).to(torch.bfloat16))
+                   for k, v in streams]
     if kind == ga.GLOBAL and capacity is None:
         capacity = max(pos0) + n
     layer = sentinel_cache(kind, B, capacity)
@@ -80,6 +85,28 @@ def test_verify_ragged(kind, n):
     assert _unchanged(layer, snap), "verify must not write the cache"
     want = _oracle_rows(kind, q, streams, pos0, list(range(n)))
     check_close(out.cpu().numpy(), want, "verify kind=%d n=%d" % (kind, n))
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+@pytest.mark.parametrize("log2c", [18, -100])
+def test_verify_value_scale(kind, log2c):
+    """Attention is linear in the values: with every value vector times
+    c = 2^log2c (exact in bf16) the output is c times the oracle's for the
+    unscaled cache, so got / c meets the usual bar.  At c = 2^18 the values
+    (up to ~10^6) lie beyond fp16's range and at c = 2^-100 far below its
+    normal range, where the key splits' 2-byte partial rows would overflow
+    or flush without their per-row scale."""
+    pos0, n = [3000, 9000], 16
+    c = 2.0 ** log2c
+    print("verify value scale kind=%d c=2^%d" % (kind, log2c), flush=True)
+    layer, streams, q, kb, vb = _setup(kind, pos0, n, seed=2060,
+                                       capacity=20000 if kind == ga.GLOBAL
+                                       else None, v_scale=c)
+    out = ga.attn_verify(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64) / c
+    want = _oracle_rows(kind, q, streams, pos0, list(range(n))) / c
+    check_close(got, want, "verify value scale kind=%d c=2^%d" % (kind, log2c))
 
 
 @pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
