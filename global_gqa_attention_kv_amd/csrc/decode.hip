@@ -925,7 +925,7 @@ template <bool F8>
 hipError_t launch_split(const DecodeParams& p, const DecodePlan& plan,
                         bool local, hipStream_t s) {
   if (local && plan.heads_per_wg == kLocalSmallHeads) {
-    // small batches: 4 workgroups (head groups) share each tile
+    // small batches: HG workgroups (head groups) share each tile
     constexpr int HG = kGroup / kLocalSmallHeads;
     const int grid = (p.units + p.xcds - 1) / p.xcds * p.xcds * HG;
     if (p.tiles_per_split != 1) return hipErrorInvalidValue;

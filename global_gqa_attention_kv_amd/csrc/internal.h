@@ -62,10 +62,12 @@ constexpr int kGlobalVRing = 2;
 // Local-layer decode (latency-bound, one tile per workgroup): 8 waves of 2
 // heads put more waves behind each tile than 4 waves of 4 heads.
 constexpr int kLocalWaves = 8;
-// Local layers at small batch: the 16 heads of a KV head split over
-// workgroups of kLocalSmallHeads heads in 2 waves, which read the same tile
-// (L2 hits after the first) and each do a quarter of the products.
-constexpr int kLocalSmallWaves = 2;
+// Local layers at small batch: the 16 heads of a KV head split over two
+// workgroups of kLocalSmallHeads = 8 heads in 4 waves, which read the same
+// tile (L2 hits after the first) and each do half of the products (measured
+// at batch 1 against four workgroups of 4 heads in 2 waves: 52-layer step at
+// 131072 keys 818 -> 799 us; one workgroup of 16 heads was slower still).
+constexpr int kLocalSmallWaves = 4;
 
 struct DecodeParams {
   const uint16_t* k;       // cache base (sequence 0, slot 0, head 0)

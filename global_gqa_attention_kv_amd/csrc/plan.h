@@ -33,7 +33,7 @@ constexpr int kDecTile = 64;               // keys per tile
 constexpr int kGlobalWGsPerCU = 2;
 // Local layers at small batch: the 16 heads of a KV head split over 4
 // workgroups (head groups) that read the same tile.
-constexpr int kLocalSmallHeads = 4;
+constexpr int kLocalSmallHeads = 8;
 constexpr int kLocalSmallMaxBatch = 2;
 // Most key splits of one decode or block call (a merge loads them all at
 // once).

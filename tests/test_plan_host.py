@@ -98,7 +98,7 @@ def test_decode_plans_cover_and_fit(plans, cus, xcds):
                         assert t == 1      # as many splits as tiles
                 else:
                     assert wgs <= max(2 * cus, 2 * B), (B, ctx, p)
-                    assert p["hpw"] == (4 if B <= 2 else 16)
+                    assert p["hpw"] == (8 if B <= 2 else 16)
                 assert p["ws"] >= B * 2 * s * 16 * 130 * 4
                 assert p["ws"] % 256 == 0
 
