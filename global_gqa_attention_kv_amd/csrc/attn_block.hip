@@ -514,9 +514,13 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
           S[be][i] = ok ? S[be][i] : -INFINITY;
         }
     }
-    float mt = fmaxf(max16(S[0]), max16(S[1]));
-    mt = xmax<32>(mt) + mb;  // tile max, log2 units
-    if (__any(mt > m_run + kTauB)) {
+    // This lane's largest score (its 16 keys of each block), log2 units.
+    // A row's two lanes (32 apart) decide together exactly as on the row
+    // maximum would (x -> x + mb is monotonic), so the exchange with the
+    // partner lane is only taken on the rare rescaling path.
+    const float ml = fmaxf(max16(S[0]), max16(S[1])) + mb;
+    if (__any(ml > m_run + kTauB)) {
+      const float mt = xmax<32>(ml);  // tile max of the row
       const float mn = fmaxf(m_run, mt);
       const float alpha = mn == m_run ? 1.0f : fast_exp2(m_run - mn);
       m_run = mn;
