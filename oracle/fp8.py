@@ -96,10 +96,39 @@ def attend(q, qpos, k_codes, k_scales, v_codes, v_scales, kpos0, *, hq, hkv,
     """Attention (as :func:`oracle.attend`) over a quantised K/V stream: row r
     of the codes / scales is position kpos0 + r.  The keys and values are the
     exact dequantised values."""
+    return _attend64(q, qpos, dequantize(k_codes, k_scales),
+                     dequantize(v_codes, v_scales), kpos0, hq=hq, hkv=hkv, d=d,
+                     window=window, rope=rope, theta=theta, scale=scale,
+                     nthreads=nthreads)
+
+
+def attend_mixed(q, qpos, k_codes, k_scales, v_codes, v_scales, k_blk, v_blk,
+                 kpos0, *, hq, hkv, d, window, rope, theta=10000.0, scale=None,
+                 nthreads=None):
+    """Attention of a block of new tokens over an fp8 cache (speculative
+    verification, page "Deep dive into Muse Glimmer", shishifenxi.com,
+    section 04: the main model checks a drafted block in one pass).  The
+    stream's first rows are cached tokens, read as their exact dequantised
+    values (codes / scales [nc, hkv, d] / [nc, hkv], positions kpos0 ..
+    kpos0+nc-1); the block's own tokens follow (k_blk, v_blk bf16 bits
+    [n, hkv, d] at positions kpos0+nc ..) and enter with their bf16 values:
+    they arrive with the call and are not in the cache yet, so nothing has
+    quantised them.  Queries q [nq, hq, d] at positions qpos."""
+    kb = _as_f32_bf16(k_blk).reshape(-1, hkv, d).astype(np.float64)
+    vb = _as_f32_bf16(v_blk).reshape(-1, hkv, d).astype(np.float64)
+    k = np.concatenate([dequantize(k_codes, k_scales).reshape(-1, hkv, d), kb])
+    v = np.concatenate([dequantize(v_codes, v_scales).reshape(-1, hkv, d), vb])
+    return _attend64(q, qpos, k, v, kpos0, hq=hq, hkv=hkv, d=d, window=window,
+                     rope=rope, theta=theta, scale=scale, nthreads=nthreads)
+
+
+def _attend64(q, qpos, k, v, kpos0, *, hq, hkv, d, window, rope, theta,
+              scale, nthreads):
+    """The oracle's attention on float64 keys and values."""
     from oracle import _bits, _cfg, _load, _nthreads, _ptr, OracleRangeError
     q = _bits(q).reshape(-1, hq, d)
-    k = np.ascontiguousarray(dequantize(k_codes, k_scales), dtype=np.float64)
-    v = np.ascontiguousarray(dequantize(v_codes, v_scales), dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
     qpos = np.ascontiguousarray(qpos, dtype=np.int64).reshape(-1)
     nq, nk = q.shape[0], k.shape[0]
     out = np.zeros((nq, hq, d), dtype=np.float64)

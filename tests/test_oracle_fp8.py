@@ -14,7 +14,10 @@ representability, the rounding error bound, exact power-of-two rescaling
 and sign symmetry, and attention over the dequantised cache against an
 independent numpy brute force.  Planted mistakes in a copy of the module
 (ties away from zero, truncation, a wrong maximum, a shifted subnormal
-step, a lost sign, no clamp, a wrong exponent bias) are each caught."""
+step, a lost sign, no clamp, a wrong exponent bias) are each caught.
+Attention of a block of new bf16 tokens over the fp8 cache (verification)
+is pinned by the same brute force on the concatenated stream, by a closed
+form with a zero prior, and by the bf16 oracle on exactly held caches."""
 import importlib.util
 import math
 
@@ -278,3 +281,94 @@ def test_fp8_mutant_is_caught(name, tmp_path):
         except (AssertionError, ValueError):
             caught.append(pin.__name__)
     assert caught, "no pin caught mutant %s" % name
+
+
+# ------------------------- a block of new tokens over the cache (verify)
+
+def _mixed_stream(seed, nc, n, hkv=2, d=16):
+    """An fp8 prior stream of nc cached tokens (quantised from bf16 rows) and
+    n new bf16 tokens."""
+    kb = si.bits(si.randn_bf16((nc, hkv, d), seed=seed))
+    vb = si.bits(si.randn_bf16((nc, hkv, d), seed=seed + 1))
+    kn = si.bits(si.randn_bf16((n, hkv, d), seed=seed + 2))
+    vn = si.bits(si.randn_bf16((n, hkv, d), seed=seed + 3))
+    kc, ks = fp8_mod.quantize(kb, hkv, d)
+    vc, vs = fp8_mod.quantize(vb, hkv, d)
+    return kc, ks, vc, vs, kn, vn
+
+
+@pytest.mark.parametrize("window,rope", [(0, False), (8, True), (5, False)])
+def test_attend_mixed_bruteforce(window, rope):
+    """Queries of a block at positions kpos0+nc .. against the dequantised
+    prior then the block's own bf16 keys, causal inside the block: the numpy
+    brute force on the concatenated float stream."""
+    hq, hkv, d, nc, n = 8, 2, 16, 30, 6
+    kpos0 = 4 if window else 0  # a global query needs every key from 0
+    kc, ks, vc, vs, kn, vn = _mixed_stream(71, nc, n, hkv, d)
+    qb = si.bits(si.randn_bf16((n, hq, d), seed=75))
+    qpos = kpos0 + nc + np.arange(n)
+    got = fp8_mod.attend_mixed(qb, qpos, kc, ks, vc, vs, kn, vn, kpos0, hq=hq,
+                               hkv=hkv, d=d, window=window, rope=rope)
+    k = np.concatenate([fp8_mod.dequantize(kc, ks), _f(kn)])
+    v = np.concatenate([fp8_mod.dequantize(vc, vs), _f(vn)])
+    want = _brute64(_f(qb), qpos, k, v, kpos0, hq, hkv, window, rope)
+    assert np.abs(got - want).max() < 1e-12
+
+
+def test_attend_mixed_block_enters_unquantised():
+    """The block's rows are taken at their bf16 values: quantising them too
+    changes the result, and the last query attends to its own key and value
+    exactly as the brute force on bf16 block rows says."""
+    hq, hkv, d, nc, n = 8, 2, 16, 20, 4
+    kc, ks, vc, vs, kn, vn = _mixed_stream(81, nc, n, hkv, d)
+    qb = si.bits(si.randn_bf16((n, hq, d), seed=85))
+    qpos = nc + np.arange(n)
+    got = fp8_mod.attend_mixed(qb, qpos, kc, ks, vc, vs, kn, vn, 0, hq=hq,
+                               hkv=hkv, d=d, window=0, rope=False)
+    knc, kns = fp8_mod.quantize(kn, hkv, d)
+    vnc, vns = fp8_mod.quantize(vn, hkv, d)
+    allq = fp8_mod.attend(qb, qpos, np.concatenate([kc, knc]),
+                          np.concatenate([ks, kns]), np.concatenate([vc, vnc]),
+                          np.concatenate([vs, vns]), 0, hq=hq, hkv=hkv, d=d,
+                          window=0, rope=False)
+    assert np.abs(got - allq).max() > 1e-4
+    # with a prior of zero scales (zero keys and values) the first query
+    # weighs its nc + 1 keys equally except its own, whose score is exact
+    zs = np.zeros_like(ks)
+    got0 = fp8_mod.attend_mixed(qb, qpos, kc, zs, vc, zs, kn, vn, 0, hq=hq,
+                                hkv=hkv, d=d, window=0, rope=False)
+    q0 = _f(qb)[0]
+    g = np.repeat(np.arange(hkv), hq // hkv)
+    s = (q0 * _f(kn)[0][g]).sum(-1) / math.sqrt(d)
+    w = np.exp(s) / (nc + np.exp(s))
+    assert np.abs(got0[0] - w[:, None] * _f(vn)[0][g]).max() < 1e-12
+
+
+def test_attend_mixed_equals_bf16_attend_when_exact():
+    """A prior made of E4M3 values times 2^-6 (largest 7, so scale 2^-6) is
+    held exactly: the mixed attention equals the bf16 oracle's attention on
+    the prior's bf16 values followed by the block."""
+    import torch
+    rng = np.random.default_rng(91)
+    table = fp8_mod.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+    nc, n, hq, hkv, d = 48, 16, 32, 2, 128
+    prior = []
+    for _ in range(2):
+        vals = rng.choice(table, size=(nc, hkv, d)) * \
+            rng.choice([-1, 1], (nc, hkv, d)) * 2.0 ** -6
+        vals[:, :, 0] = 7.0
+        prior.append(si.bits(torch.from_numpy(vals).to(torch.bfloat16)))
+    kn = si.bits(si.randn_bf16((n, hkv, d), seed=92))
+    vn = si.bits(si.randn_bf16((n, hkv, d), seed=93))
+    qb = si.bits(si.randn_bf16((n, hq, d), seed=94))
+    kc, ks = fp8_mod.quantize(prior[0])
+    vc, vs = fp8_mod.quantize(prior[1])
+    for window, rope in ((0, False), (16, True)):
+        kpos0 = 100 if window else 0  # a global query needs every key from 0
+        qpos = kpos0 + nc + np.arange(n)
+        a = fp8_mod.attend_mixed(qb, qpos, kc, ks, vc, vs, kn, vn, kpos0,
+                                 hq=hq, hkv=hkv, d=d, window=window, rope=rope)
+        b = oracle.attend(qb, qpos, np.concatenate([prior[0], kn]),
+                          np.concatenate([prior[1], vn]), kpos0, hq=hq,
+                          hkv=hkv, d=d, window=window, rope=rope)
+        assert np.abs(a - b).max() < 1e-12
