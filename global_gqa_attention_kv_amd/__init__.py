@@ -21,7 +21,8 @@ __all__ = [
     "MAX_VERIFY", "attn_verify", "attn_draft_block", "attn_prefill", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
     "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
     "attn_decode", "attn_decode_append", "attn_decode_dev",
-    "attn_decode_noalloc", "LayerFp8", "kv_append_fp8", "attn_decode_fp8", "workspace_bytes", "workspace", "status_string", "abi_version",
+    "attn_decode_noalloc", "LayerFp8", "kv_append_fp8", "attn_decode_fp8",
+    "attn_verify_fp8", "attn_draft_block_fp8", "workspace_bytes", "workspace", "status_string", "abi_version",
     "library_path", "layer_kind", "NUM_LAYERS",
 ]
 
@@ -111,6 +112,10 @@ def _load():
         lib.gqa_attn_decode_fp8.restype = i32
         lib.gqa_attn_decode_fp8.argtypes = [L8, p, p, i32, p, p,
                                             ctypes.c_size_t, p]
+        for name in ("gqa_attn_verify_fp8", "gqa_attn_draft_block_fp8"):
+            f = getattr(lib, name)
+            f.restype = i32
+            f.argtypes = [L8, p, p, p, p, i32, i32, p, p, ctypes.c_size_t, p]
         lib.gqa_attn_decode_noalloc.restype = i32
         lib.gqa_attn_decode_noalloc.argtypes = [L, p, p, p, p, i32, p, p]
         _lib = lib
@@ -431,6 +436,24 @@ def attn_verify(layer: Layer, q, k_blk, v_blk, pos0, out=None, ws=None,
     return _block_common(_load().gqa_attn_verify, "gqa_attn_verify",
                          OP_VERIFY, torch.float32, layer, q, k_blk, v_blk,
                          pos0, out, ws, stream)
+
+
+def attn_verify_fp8(layer: LayerFp8, q, k_blk, v_blk, pos0, out=None,
+                    ws=None, stream=None):
+    """:func:`attn_verify` over an fp8 cache: the cached tokens are read as
+    their dequantised values, the block's own tokens (k_blk, v_blk bf16, not
+    in the cache) at their bf16 values.  Returns fp32 [B, n, 32, 128]."""
+    return _block_common(_load().gqa_attn_verify_fp8, "gqa_attn_verify_fp8",
+                         OP_VERIFY, torch.float32, layer, q, k_blk, v_blk,
+                         pos0, out, ws, stream)
+
+
+def attn_draft_block_fp8(layer: LayerFp8, q, k_blk, v_blk, pos0, out=None,
+                         ws=None, stream=None):
+    """:func:`attn_draft_block` over an fp8 cache (global layers)."""
+    return _block_common(_load().gqa_attn_draft_block_fp8,
+                         "gqa_attn_draft_block_fp8", OP_DRAFT, torch.float32,
+                         layer, q, k_blk, v_blk, pos0, out, ws, stream)
 
 
 def attn_draft_block(layer: Layer, q, k_blk, v_blk, pos0, out=None, ws=None,

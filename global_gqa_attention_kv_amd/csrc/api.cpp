@@ -80,8 +80,14 @@ size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx) {
       const bool verify = op != GQA_OP_PREFILL;
       if (n > (verify ? GQA_MAX_VERIFY : GQA_MAX_CONTEXT)) return 0;
       const int64_t keys = visible_keys(kind, max_ctx - 1);
-      return block_ws_bytes(
-          plan_block(kind, B, n, keys, current_device_shape()));
+      const DeviceShape dev = current_device_shape();
+      const size_t need = block_ws_bytes(plan_block(kind, B, n, keys, dev));
+      if (!verify) return need;
+      // one verify workspace serves both cache formats (fp8 calls always
+      // split their keys)
+      const size_t need8 =
+          block_ws_bytes(plan_block(kind, B, n, keys, dev, true));
+      return need > need8 ? need : need8;
     }
     default:
       return 0;
@@ -324,6 +330,71 @@ int gqa_attn_draft_block(const gqa_layer* layer, const void* q,
                          void* ws, size_t ws_bytes, void* stream) {
   return block_impl(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
                     true, true, stream);
+}
+
+// Verification or a drafted block over an fp8 cache.
+static int block_impl_fp8(const gqa_layer_fp8* layer, const void* q,
+                          const void* k_blk, const void* v_blk,
+                          const int64_t* pos0, int B, int n, float* out,
+                          void* ws, size_t ws_bytes, bool together,
+                          void* stream) {
+  int64_t max_keys = 0;
+  int rc = check_block_fp8(layer, q, k_blk, v_blk, pos0, B, n, out,
+                           &max_keys);
+  if (rc != GQA_OK) return rc;
+  if (together && layer->kind != GQA_GLOBAL) return GQA_ERR_UNSUPPORTED;
+  const BlockPlan plan =
+      plan_block(layer->kind, B, n, max_keys, current_device_shape(), true);
+  if (!ws) return GQA_ERR_INVALID_ARG;
+  if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
+  if (ws_bytes < block_ws_bytes(plan)) return GQA_ERR_WS_TOO_SMALL;
+  BlockParams p;
+  memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_blk = static_cast<const uint16_t*>(k_blk);
+  p.v_blk = static_cast<const uint16_t*>(v_blk);
+  p.k8 = static_cast<const uint8_t*>(layer->k);
+  p.v8 = static_cast<const uint8_t*>(layer->v);
+  p.k_scale = layer->k_scale;
+  p.v_scale = layer->v_scale;
+  p.scale_stride = layer->scale_stride;
+  p.capacity = layer->capacity;
+  p.part = reinterpret_cast<float*>(ws);
+  p.out = out;
+  p.seq_stride = layer->seq_stride;  // bytes of codes per sequence
+  p.n = n;
+  p.qgroups = plan.qgroups;
+  p.qpw = plan.qpw;
+  p.splits = plan.splits;
+  p.batch = B;
+  p.together = together ? 1 : 0;
+  p.scale_log2 = (float)(1.0 / sqrt((double)kD) * 1.4426950408889634);
+  const bool local = layer->kind == GQA_LOCAL;
+  if (local) {
+    for (int c = 0; c < kD / 2; ++c)
+      p.rope_rev[c] = (float)(pow(layer->rope_theta, -(double)c / (kD / 2)) /
+                              (2.0 * 3.14159265358979323846));
+  }
+  for (int b = 0; b < B; ++b) p.pos0[b] = pos0[b];
+  hipError_t e =
+      launch_block(p, plan, local, true, B, (hipStream_t)stream, true);
+  return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_attn_verify_fp8(const gqa_layer_fp8* layer, const void* q,
+                        const void* k_blk, const void* v_blk,
+                        const int64_t* pos0, int B, int n, float* out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return block_impl_fp8(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
+                        false, stream);
+}
+
+int gqa_attn_draft_block_fp8(const gqa_layer_fp8* layer, const void* q,
+                             const void* k_blk, const void* v_blk,
+                             const int64_t* pos0, int B, int n, float* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return block_impl_fp8(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
+                        true, stream);
 }
 
 int gqa_attn_prefill(const gqa_layer* layer, const void* q,

@@ -75,6 +75,39 @@ constexpr int kPartRow = 68;
 // the exponent e is clamped so both scales stay normal fp32 numbers (rows
 // below 2^-100 keep their absolute error far under any bf16 rounding)
 constexpr int kPartExpMin = -100;
+// fp8 caches (verification and drafted blocks, key splits only): code tiles
+// (64 rows of one KV head's 128 E4M3 codes for K, then for V) and their
+// rows' scales stream into a ring of kRing slots; each wave turns its own
+// rows of a landed tile into bf16 codes in one of two staging slots laid out
+// as the bf16 ring slots are, so the products run unchanged on them, and
+// the scores take the K scales and the weights the V scales.  The block's
+// own tokens (bf16, not in the cache) sit in LDS for the whole call.
+constexpr int kCodeTileB = kBlkTile * kD;               // 8 KB of codes
+constexpr int kCodeSlotB = 2 * kCodeTileB;              // K codes, V codes
+constexpr int kScaleSlotB = 2 * kBlkTile * 4;           // 64 K, 64 V scales
+constexpr int kF8Codes = 2 * kSlotB;                    // after the staging
+constexpr int kF8BlkRows = GQA_MAX_VERIFY;
+// LDS of the fp8 variant with `waves` waves: staging, code ring, then the
+// scale ring (per slot, for K then V, each wave's 64 scale words: lane l
+// the scale of its row l % (64 / waves)), the staging scales, the block's
+// rows and (local layers) the query RoPE table.
+struct F8Lds {
+  int raw, raw_slot, st_sc, blk, rtab, size;
+};
+constexpr F8Lds f8_lds(int waves, int qpw, bool local) {
+  F8Lds l{};
+  l.raw_slot = 2 * waves * 256;
+  l.raw = kF8Codes + kRing * kCodeSlotB;
+  l.st_sc = l.raw + kRing * l.raw_slot;
+  l.blk = l.st_sc + 2 * kScaleSlotB;
+  l.rtab = l.blk + 2 * kF8BlkRows * 256;
+  l.size = l.rtab + (local ? qpw * 32 * 16 : 0);
+  return l;
+}
+static_assert(f8_lds(kBlkQpw / 2, kBlkQpw, false).size <= 160 * 1024 &&
+                  f8_lds(kBlkQpwSmall / 2, kBlkQpwSmall, true).size <=
+                      160 * 1024,
+              "fp8 block kernel LDS");
 
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -123,6 +156,27 @@ __device__ __forceinline__ void dma16(const uint16_t* base, uint32_t off,
       : "=&s"(saved)
       : "v"(off), "s"(base), "s"(lds)
       : "memory");
+}
+// Direct-to-LDS load of 4 bytes per active lane (lane l's word lands at
+// lds + 4 l); lanes outside the exec mask load nothing.
+__device__ __forceinline__ void dma4(const float* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+// Two E4M3 codes (the lower or upper half of w, first code in the lower
+// byte) as a bf16 pair, exactly (every E4M3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 __device__ __forceinline__ void wait_vmcnt0() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -206,15 +260,18 @@ __device__ __forceinline__ float max16(const f32x16_t& v) {
 // keys hit distinct banks; V chunk c at slot c ^ X(r & 3), X = {0, 4, 10,
 // 14}: the four keys of a 16-lane group of ds_read_b64_tr_b16, and the 64
 // bytes of each key read by a 32-lane half, land on distinct banks.
-template <int QPW, bool LOCAL, bool SPLIT, bool OUT_F32>
+template <int QPW, bool LOCAL, bool SPLIT, bool OUT_F32, bool F8 = false>
 __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
     const BlockParams p) {
+  static_assert(!F8 || SPLIT, "fp8 caches: key-split calls only");
+  constexpr F8Lds L8 = f8_lds(QPW / 2, QPW, LOCAL);
   constexpr int WAVES = QPW / 2;  // waves of 32 rows (2 tokens x 16 heads)
   constexpr int RING = kRing;
   constexpr int ROWS = QPW * kGroup;
   constexpr int RPW = kBlkTile / WAVES;   // tile rows each wave loads
   constexpr int LPT = RPW / 4;            // 1-KB loads per K or V tile per wave
-  __shared__ __attribute__((aligned(16))) uint8_t smem[RING * kSlotB];
+  __shared__ __attribute__((aligned(16))) uint8_t
+      smem[F8 ? L8.size : RING * kSlotB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -276,7 +333,8 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
   // the 16 lanes of a token (one per head) then read them instead of each
   // evaluating its own.  Entry 32 t + j holds (sin, cos) of frequencies 2j
   // and 2j + 1 at token q_first + t.
-  float4* const rtab = reinterpret_cast<float4*>(smem + (RING - 1) * kSlotB);
+  float4* const rtab = reinterpret_cast<float4*>(
+      smem + (F8 ? L8.rtab : (RING - 1) * kSlotB));
   if constexpr (LOCAL) {
     static_assert(WAVES * 64 == QPW * 32, "one table entry per thread");
     const int t = tid >> 5, j = tid & 31;
@@ -418,6 +476,132 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
     }
   };
 
+  // ---- fp8 caches.  Codes: sequence b at byte b * seq_stride, rows of
+  // 2 x 128 codes; scales [B][2][capacity].  Wave w loads code rows
+  // RPW w .. RPW (w+1) - 1 of tile t into ring slot t % RING (lane l: row
+  // RPW w + 8i + l / 8, codes 16 (l % 8) .. + 15) and the rows' K and V
+  // scales (lane l: row RPW w + l % RPW; every lane loads, as a
+  // direct-to-LDS load places lane l's word at its base + 4 l).  Rows at
+  // block positions (not cached yet)
+  // read the slot they map to and are replaced from the block's rows when
+  // dequantised; rows past the range repeat its last key (masked).
+  constexpr int LPT8 = RPW / 8;         // 1-KB code loads per K (V) tile
+  constexpr int LPI8 = 2 * LPT8 + 2;    // loads of one tile per wave
+  const uint8_t* k8_base = p.k8 + (int64_t)b * p.seq_stride + g * kD;
+  const uint8_t* v8_base = p.v8 + (int64_t)b * p.seq_stride + g * kD;
+  const float* ks_base =
+      p.k_scale + (int64_t)b * p.scale_stride + (int64_t)g * p.capacity;
+  const float* vs_base =
+      p.v_scale + (int64_t)b * p.scale_stride + (int64_t)g * p.capacity;
+  const int crow = lane >> 3, cch = lane & 7;
+  auto slot8 = [](int j) { return LOCAL ? (j & (kW - 1)) : j; };
+  auto issue_tile8 = [&](int t, auto SLOT) {
+    const int kb = k_lo + (t_begin + t) * kBlkTile;
+    const uint32_t cb = __builtin_amdgcn_readfirstlane(
+        lds_base + kF8Codes + SLOT * kCodeSlotB + RPW * w * kD);
+#pragma unroll
+    for (int i = 0; i < LPT8; ++i) {
+      const int j = min(kb + RPW * w + 8 * i + crow, k_hi - 1);
+      const int64_t off = (int64_t)slot8(j) * kTokenElems + cch * 16;
+      dma16(reinterpret_cast<const uint16_t*>(k8_base + off), cb + i * 1024);
+      dma16(reinterpret_cast<const uint16_t*>(v8_base + off),
+            cb + kCodeTileB + i * 1024);
+    }
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(
+        lds_base + L8.raw + SLOT * L8.raw_slot + w * 256);
+    const int j = min(kb + RPW * w + lane % RPW, k_hi - 1);
+    dma4(ks_base + slot8(j), sb);
+    dma4(vs_base + slot8(j), sb + WAVES * 256);
+  };
+  // Wave w's own rows of the landed tile in ring slot SLOT -> bf16 codes in
+  // staging slot ST (exact), in the swizzled layouts the products read; a
+  // row at a block position takes the block's bf16 row instead.  Lane l of
+  // a row writes dims 16 (l % 8) .. + 15; lane 0 of the row its K and V
+  // scales (1 for block rows) to the staging scales.
+  auto dequant8 = [&](int t, auto SLOT, auto ST) {
+    const int kb = k_lo + (t_begin + t) * kBlkTile;
+    static_for<0, LPT8>([&](auto I) {
+      const int r = RPW * w + 8 * I + crow;
+      const int j = min(kb + r, k_hi - 1);
+      const bool blk = j >= pos0;
+      static_for<0, 2>([&](auto IV) {
+        u32x4_t lo, hi;
+        if (blk) {
+          const uint32_t src = lds_base + L8.blk +
+                               (IV * kF8BlkRows + (j - pos0)) * 256 + cch * 32;
+          lo = *reinterpret_cast<const lds_u32x4_t*>(src);
+          hi = *reinterpret_cast<const lds_u32x4_t*>(src + 16);
+        } else {
+          const u32x4_t c = *reinterpret_cast<const lds_u32x4_t*>(
+              lds_base + kF8Codes + SLOT * kCodeSlotB + IV * kCodeTileB +
+              r * kD + cch * 16);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            lo[2 * e] = cvt_fp8x2_bf16<false>(c[e]);
+            lo[2 * e + 1] = cvt_fp8x2_bf16<true>(c[e]);
+            hi[2 * e] = cvt_fp8x2_bf16<false>(c[e + 2]);
+            hi[2 * e + 1] = cvt_fp8x2_bf16<true>(c[e + 2]);
+          }
+        }
+        const int swz = IV ? vswz(r) : (r & 15);
+        const uint32_t dst = lds_base + ST * kSlotB + IV * kTileB + r * 256;
+        *reinterpret_cast<lds_u32x4_t*>(dst + (((2 * cch) ^ swz) << 4)) = lo;
+        *reinterpret_cast<lds_u32x4_t*>(dst + (((2 * cch + 1) ^ swz) << 4)) =
+            hi;
+      });
+      if (cch == 0) {
+        // this row's scale words: wave w's lane r - RPW w
+        const float* raw = reinterpret_cast<const float*>(
+            smem + L8.raw + SLOT * L8.raw_slot + w * 256 + 4 * (r - RPW * w));
+        float* st = reinterpret_cast<float*>(smem + L8.st_sc + ST * kScaleSlotB);
+        st[r] = blk ? 1.0f : raw[0];
+        st[kBlkTile + r] = blk ? 1.0f : raw[WAVES * 64];
+      }
+    });
+  };
+  // Local layers: each wave rotates its own rows of the staging K tile by
+  // their keys' offsets from p0 (item i: row RPW w + 8i + l / 8, dims
+  // 8 (l % 8) .. + 7 against 64 + 8 (l % 8) ..); the angles are taken while
+  // the tile is in flight.
+  float rc8[LPT8][8], rs8[LPT8][8];
+  auto rope_angles8 = [&](int t) {
+    const int kb = k_lo + (t_begin + t) * kBlkTile;
+#pragma unroll
+    for (int i = 0; i < LPT8; ++i) {
+      const int j = min(kb + RPW * w + 8 * i + crow, k_hi - 1);
+      const float delta = (float)(j - pos0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float rr = delta * p.rope_rev[cch * 8 + e];
+        rr -= rintf(rr);
+        sincos_rev(rr, &rs8[i][e], &rc8[i][e]);
+      }
+    }
+  };
+  auto rope_own = [&](auto ST) {
+#pragma unroll
+    for (int i = 0; i < LPT8; ++i) {
+      const int r = RPW * w + 8 * i + crow;
+      const uint32_t rb = lds_base + ST * kSlotB + r * 256;
+      lds_u32x4_t* lo =
+          reinterpret_cast<lds_u32x4_t*>(rb + ((cch ^ (r & 15)) << 4));
+      lds_u32x4_t* hi =
+          reinterpret_cast<lds_u32x4_t*>(rb + (((cch + 8) ^ (r & 15)) << 4));
+      u32x4_t a = *lo, c = *hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = bf16_lo(a[e]), x1 = bf16_hi(a[e]);
+        const float y0 = bf16_lo(c[e]), y1 = bf16_hi(c[e]);
+        const float c0 = rc8[i][2 * e], s0 = rs8[i][2 * e];
+        const float c1 = rc8[i][2 * e + 1], s1 = rs8[i][2 * e + 1];
+        a[e] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+        c[e] = pack_bf16(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+      }
+      *lo = a;
+      *hi = c;
+    }
+  };
+
   // LDS read addresses.  K operand of k-step k: key 32be + row, chunk
   // 2k + hi5 (+ 8192 B for be = 1).  V^T operand of dim block d: the
   // 16-lane group G (keys + 4(G >> 1), dims + 16(G & 1)) transposes keys
@@ -455,6 +639,10 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
     // it has none; the first product of each block adds onto the constant
     // vector negmb), so they end up holding s - mb in log2 units.
     const float mb = -negmb[0];
+    // fp8: the products start from zero and take their keys' K scales below
+    f32x16_t acc0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc0[i] = F8 ? 0.0f : negmb[i];
     f32x16_t S[2];
     bf16x8_t ka[2][8];
 #pragma unroll
@@ -463,13 +651,13 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          ka[0][k], qreg[k], k == 0 ? negmb : S[0], 0, 0, 0);
+          ka[0][k], qreg[k], k == 0 ? acc0 : S[0], 0, 0, 0);
       ka[1][k] = *reinterpret_cast<const lds_bf16x8_t*>(krd[k] + so + 8192);
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          ka[1][k], qreg[k], k == 0 ? negmb : S[1], 0, 0, 0);
+          ka[1][k], qreg[k], k == 0 ? acc0 : S[1], 0, 0, 0);
     // The V^T operands of the first 16-key step of P.V are requested
     // meanwhile (they do not depend on the softmax).
     constexpr uint32_t vo = so;  // vrd[] already points into the V tile
@@ -496,6 +684,26 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     });
 
+    // fp8: score s = product x (its key's K scale) - mb; the lane's keys of
+    // block be, entry 4 qd + e, are 32 be + 8 qd + 4 hi5 + e
+    const uint32_t scb = lds_base + L8.st_sc + SLOT * kScaleSlotB + 16 * hi5;
+    if constexpr (F8) {
+#pragma unroll
+      for (int be = 0; be < 2; ++be)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const u32x4_t k4 = *reinterpret_cast<const lds_u32x4_t*>(
+              scb + 4 * (32 * be + 8 * qd));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // the element goes through a scalar: a bit cast taken directly
+            // on a vector element reads element 0 with this compiler
+            const uint32_t kw = k4[e];
+            S[be][4 * qd + e] =
+                fmaf(S[be][4 * qd + e], __builtin_bit_cast(float, kw), -mb);
+          }
+        }
+    }
     // ---- softmax update for this lane's row.  The maximum is taken on raw
     // scores, already scaled to log2 units and shifted by -mb: p = 2^(S).
     const int kb = k_lo + (t_begin + t) * kBlkTile;
@@ -550,16 +758,33 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
     for (int be = 0; be < 2; ++be)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        uint32_t w4[4];
+        uint32_t w4[4], pv[4];
+        // fp8: the V scales of keys 32 be + 8 (2 tt + h) + 4 hi5 + 0..3
+        u32x4_t v4[2];
+        if constexpr (F8) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            v4[h] = *reinterpret_cast<const lds_u32x4_t*>(
+                scb + 4 * (kBlkTile + 32 * be + 8 * (2 * tt + h)));
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float p0 = fast_exp2(S[be][8 * tt + 2 * j]);
           const float p1 = fast_exp2(S[be][8 * tt + 2 * j + 1]);
           w4[j] = pack_bf16(p0, p1);
           lp[j] = dot2_bf16(w4[j], 0x3F803F80u, lp[j]);
+          if constexpr (F8) {
+            // the weight times its key's V scale, rounded once
+            const uint32_t v0 = v4[j >> 1][2 * (j & 1)];
+            const uint32_t v1 = v4[j >> 1][2 * (j & 1) + 1];
+            pv[j] = pack_bf16(p0 * __builtin_bit_cast(float, v0),
+                              p1 * __builtin_bit_cast(float, v1));
+          } else {
+            pv[j] = w4[j];
+          }
         }
         P[2 * be + tt] = __builtin_bit_cast(
-            bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+            bf16x8_t, make_uint4(pv[0], pv[1], pv[2], pv[3]));
       }
     l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
 
@@ -636,6 +861,55 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
     }
   };
 
+  if constexpr (F8) {
+    // the block's bf16 K and V rows of this KV head (rows n .. 15 repeat
+    // the last), 8 KB, then the first code tiles; the block rows are
+    // waited for and published before any wave dequantises
+    static_for<0, 8 / WAVES>([&](auto I) {
+      const int u = (I * WAVES + w) * 64 + lane;  // 16-byte chunk of the 8 KB
+      const int rr = u >> 4, ch = u & 15;         // K rows 0..15, V 16..31
+      const int tok = min(rr & 15, p.n - 1);
+      const uint16_t* src = ((rr >> 4) ? p.v_blk : p.k_blk) +
+                            ((int64_t)b * p.n + tok) * kTokenElems + g * kD +
+                            ch * 8;
+      dma16(src, lds_base + L8.blk + (I * WAVES + w) * 1024);
+    });
+    static_for<0, RING - 1>([&](auto T) {
+      if (T < ntiles) issue_tile8(T, T);
+    });
+    {
+      const int issued = min(RING - 1, ntiles);
+      static_for<0, RING>([&](auto L) {
+        if (issued == L) wait_vmcnt<L * LPI8>();
+      });
+    }
+    __syncthreads();
+    // tile t: codes in ring slot t % RING, bf16 in staging slot t % 2.  The
+    // barrier after the dequantisation publishes the staging slot; every
+    // wave has then finished the tile before (the other staging slot's
+    // previous user, t - 2, was consumed before the last barrier) and the
+    // code slot of t - 1, which the next tile's loads reuse.
+    for (int t0 = 0; t0 < ntiles; t0 += RING) {
+      static_for<0, RING>([&](auto S) {
+        const int t = t0 + S;
+        constexpr auto ST = std::integral_constant<int, S % 2>{};
+        if (t < ntiles) {
+          if constexpr (LOCAL) rope_angles8(t);
+          const int later = min(RING - 2, ntiles - 1 - t);
+          static_for<0, RING - 1>([&](auto L) {
+            if (later == L) wait_vmcnt<L * LPI8>();
+          });
+          dequant8(t, S, ST);
+          if constexpr (LOCAL) rope_own(ST);
+          __syncthreads();
+          if (t + RING - 1 < ntiles)
+            issue_tile8(t + RING - 1,
+                        std::integral_constant<int, (S + RING - 1) % RING>{});
+          consume(t, ST);
+        }
+      });
+    }
+  } else {
   // tile t -> slot t % RING, loaded RING - 1 tiles ahead; the loop is
   // unrolled RING times so every slot offset is a constant
   static_for<0, RING - 1>([&](auto T) {
@@ -665,6 +939,7 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
       }
     });
   }
+  }  // bf16 cache
 
   // ---- epilogue: this lane holds row `row`, dims 32d + 8(i>>2) + 4 hi5 + i&3
   const float l_tot = xsum<32>(l_run);
@@ -844,8 +1119,37 @@ hipError_t launch_main(const BlockParams& p, const BlockPlan& plan, int B,
 
 }  // namespace
 
+// fp8 caches: the key-split kernels (for any split count) and the merge.
+static hipError_t launch_block_fp8(const BlockParams& p, const BlockPlan& plan,
+                            bool local, int B, hipStream_t s) {
+  if (plan.walks != 1 || plan.klin_bytes != 0 || p.part == nullptr ||
+      p.n > kF8BlkRows || p.splits > kBlkMaxSplits ||
+      plan.grid != p.splits * p.qgroups * kHkv * B || p.qpw != plan.qpw)
+    return hipErrorInvalidValue;
+  // local layers take 8-token workgroups, global layers 16
+  const dim3 grid(plan.grid);
+  if (plan.qpw != (local ? kBlkQpwSmall : kBlkQpw)) return hipErrorInvalidValue;
+  if (local)
+    hipLaunchKernelGGL(
+        (block_attn_kernel<kBlkQpwSmall, true, true, true, true>), grid,
+        dim3(kBlkQpwSmall * 32), 0, s, p);
+  else
+    hipLaunchKernelGGL((block_attn_kernel<kBlkQpw, false, true, true, true>),
+                       grid, dim3(kBlkQpw * 32), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((block_merge_kernel<true>), dim3(B * p.n * kHq), dim3(64),
+                     0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
-                        bool local, bool out_f32, int B, hipStream_t s) {
+                        bool local, bool out_f32, int B, hipStream_t s,
+                        bool fp8) {
+  if (fp8) {
+    if (!out_f32) return hipErrorInvalidValue;
+    return launch_block_fp8(p, plan, local, B, s);
+  }
   // 8-token workgroups only for local layers with key splits
   const bool small = local && p.splits > 1 && plan.qpw == kBlkQpwSmall;
   if ((plan.qpw != kBlkQpw && !small) || p.qpw != plan.qpw ||

@@ -133,9 +133,20 @@ struct BlockParams {
   int32_t qpw;              // query tokens per workgroup (the plan's)
   float scale_log2;
   float rope_rev[kD / 2];
+  // fp8 caches (key-split calls): E4M3 codes (sequence b at byte
+  // b * seq_stride) and one fp32 scale per (token, KV head) [B][2][capacity]
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* k_scale;
+  const float* v_scale;
+  int64_t scale_stride;     // floats between sequences of the scales
+  int64_t capacity;         // slots per sequence (KV-head stride of the scales)
   int64_t pos0[kMaxBatch];
 };
+// fp8: the cache is read through k8 / v8 and the scales; the plan must come
+// from plan_block(..., always_split = true).
 hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
-                        bool local, bool out_f32, int B, hipStream_t s);
+                        bool local, bool out_f32, int B, hipStream_t s,
+                        bool fp8 = false);
 
 }  // namespace gqa

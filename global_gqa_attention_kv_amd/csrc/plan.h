@@ -73,8 +73,10 @@ struct BlockPlan {
   size_t klin_bytes;   // local: pre-rotated keys
   size_t part_bytes;   // split partials
 };
+// always_split: key splits (one or more, partials and merge) whatever the
+// shape, as calls over fp8 caches take.
 BlockPlan plan_block(int kind, int B, int n, int64_t max_keys,
-                     const DeviceShape& dev);
+                     const DeviceShape& dev, bool always_split = false);
 size_t block_ws_bytes(const BlockPlan& plan);
 
 }  // namespace gqa

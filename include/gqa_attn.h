@@ -301,6 +301,33 @@ int gqa_attn_decode_fp8(const gqa_layer_fp8* layer, const void* q,
                         const int64_t* pos, int B, float* out, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* gqa_attn_verify over an fp8 cache: n (1..GQA_MAX_VERIFY) drafted tokens
+ * per sequence at positions pos0[b] .. pos0[b]+n-1, causal inside the
+ * block, attending to the cached tokens as their dequantised values
+ * (code * scale) and to the block's own tokens at their bf16 values (k_blk,
+ * v_blk [B][n][2][128] bf16: not in the cache yet, so not quantised; append
+ * the accepted ones with gqa_kv_append_fp8 afterwards).  q [B][n][32][128]
+ * bf16, out [B][n][32][128] fp32; workspace
+ * gqa_workspace_bytes(GQA_OP_VERIFY, kind, B, n, max pos0 + n) (one verify
+ * workspace serves both cache formats); errors as gqa_attn_verify.
+ * Pages: shishifenxi.com "Deep dive into Muse Glimmer" section 04 (the main
+ * model checks a drafted block in one pass) and runtimewire.com "Narrow
+ * cache" (cache quantisation). */
+int gqa_attn_verify_fp8(const gqa_layer_fp8* layer, const void* q,
+                        const void* k_blk, const void* v_blk,
+                        const int64_t* pos0, int B, int n, float* out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* gqa_attn_draft_block over an fp8 cache (global layers): every query of
+ * the block sees the dequantised cache before the block and the whole
+ * block at its bf16 values.  Arguments, workspace
+ * (gqa_workspace_bytes(GQA_OP_DRAFT, ...)) and errors as
+ * gqa_attn_draft_block. */
+int gqa_attn_draft_block_fp8(const gqa_layer_fp8* layer, const void* q,
+                             const void* k_blk, const void* v_blk,
+                             const int64_t* pos0, int B, int n, float* out,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes an operation needs for any call on a layer of `kind` with
  * batch B, n tokens per sequence and context (keys visible to the last
  * query) at most max_ctx.  Returns 0 for invalid arguments. */

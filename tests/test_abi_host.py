@@ -356,3 +356,42 @@ def test_fp8_decode_validation(lib):
     assert call(_layer8(kind=ga.LOCAL), pos=_pos(1 << 40)) == E_POS
     need = ga.workspace_bytes(ga.OP_DECODE, ga.GLOBAL, 1, 1, 4096)
     assert call(L, pos=_pos(4095), ws_bytes=need - 1) == E_WS
+
+
+@pytest.mark.parametrize("fn", ["gqa_attn_verify_fp8",
+                                "gqa_attn_draft_block_fp8"])
+def test_fp8_block_validation(lib, fn):
+    f = getattr(lib, fn)
+    L = _layer8()
+
+    def call(layer=L, q=FAKE, kb=FAKE, vb=FAKE, pos=None, B=1, n=16,
+             out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        pos = pos if pos is not None else _pos(*([0] * B))
+        return f(ctypes.byref(layer) if layer is not None else None, q, kb, vb,
+                 pos, B, n, out, ws, ws_bytes, None)
+    assert call(layer=None) == E_ARG
+    assert call(q=None) == E_ARG
+    assert call(kb=None) == E_ARG
+    assert call(vb=None) == E_ARG
+    assert call(out=None) == E_ARG
+    assert call(n=0) == E_ARG
+    assert call(n=17) == E_ARG                          # block of at most 16
+    assert call(B=0) == E_ARG
+    assert call(ws=None) == E_ARG
+    assert call(layer=_layer8(ks=0)) == E_ARG
+    assert call(layer=_layer8(kind=5)) == E_UNS
+    assert call(kb=FAKE + 4) == E_ALN
+    assert call(layer=_layer8(vs=FAKE + 4)) == E_ALN
+    assert call(ws=FAKE + 64) == E_ALN
+    assert call(pos=_pos(4096 - 15)) == E_POS           # pos0 + n > capacity
+    assert call(pos=_pos(-1)) == E_POS
+    op = ga.OP_VERIFY if fn == "gqa_attn_verify_fp8" else ga.OP_DRAFT
+    need = ga.workspace_bytes(op, ga.GLOBAL, 1, 16, 4096)
+    assert call(pos=_pos(4080), ws_bytes=need - 1) == E_WS
+    if fn == "gqa_attn_draft_block_fp8":
+        assert call(layer=_layer8(kind=ga.LOCAL)) == E_UNS
+    else:
+        # the local workspace query covers the fp8 call's key splits
+        need = ga.workspace_bytes(op, ga.LOCAL, 1, 16, 4096)
+        assert call(layer=_layer8(kind=ga.LOCAL), pos=_pos(4080),
+                    ws_bytes=need - 1) == E_WS
