@@ -273,6 +273,7 @@ def bench_decode_fp8(ga, torch, layers, qs, outs, ws, positions, kinds,
     kms = sum(per) / len(per)
     step_bytes = kv_bytes_step(kinds, positions) // 1024 * FP8_TOKEN_BYTES
     call_bytes = B * (pos + 1) * FP8_TOKEN_BYTES
+    verify = bench_verify_fp8(ga, torch, layers, l8, kinds)
     del l8
     return {"ms_per_step": round(ms, 4),
             "kv_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 2),
@@ -284,6 +285,7 @@ def bench_decode_fp8(ga, torch, layers, qs, outs, ws, positions, kinds,
             "global_call_hbm_frac": round(call_bytes / (kms * 1e-3) / 1e9 /
                                           HBM_PEAK_GBS, 4),
             "bytes_per_token_layer": FP8_TOKEN_BYTES,
+            "verify_fp8": verify,
             "workload": "52-layer decode step over fp8 caches (E4M3 + one "
                         "fp32 scale per token and KV head), context 131072, "
                         "batch %d: fp8 append + attend per layer, HIP graph"
@@ -303,6 +305,58 @@ def pairs_block_together(pos0, n):
     """Pairs of a block of n tokens at pos0 predicted together: every token
     sees positions 0 .. pos0+n-1."""
     return n * (pos0 + n)
+
+
+def bench_verify_fp8(ga, torch, layers, l8, kinds, reps=5, seed=4004):
+    """52-layer verification of a 16-token block at 131056..131071 over the
+    fp8 caches of sequence 0 (their first 131056 positions are the prior),
+    batch 1, the same block inputs as the bf16 verification; a local and a
+    global layer are checked against the bf16 verification of the same
+    tokens (only the quantisation of the prior differs)."""
+    dev = layers[0].k.device
+    n, pos0 = 16, CTX - 16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    blk = []
+    for l in range(N_LAYERS):
+        q = torch.randn((1, n, ga.HQ, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        kb = torch.randn((1, n, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        vb = torch.randn((1, n, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
+        blk.append((q, kb, vb))
+    sub = [ga.LayerFp8(kinds[l], x.k[0:1], x.v[0:1], x.k_scale[0:1],
+                       x.v_scale[0:1]) for l, x in enumerate(l8)]
+    ws = torch.empty(max(ga.workspace_bytes(ga.OP_VERIFY, k, 1, n, CTX)
+                         for k in (ga.LOCAL, ga.GLOBAL)), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((1, n, ga.HQ, ga.D), dtype=torch.float32, device=dev)
+
+    def step():
+        for l in range(N_LAYERS):
+            q, kb, vb = blk[l]
+            ga.attn_verify_fp8(sub[l], q, kb, vb, [pos0], out, ws)
+
+    ms, _, _ = time_graph(torch, step, reps, 2)
+    for l in (kinds.index(ga.LOCAL), kinds.index(ga.GLOBAL)):
+        q, kb, vb = blk[l]
+        a = ga.attn_verify_fp8(sub[l], q, kb, vb, [pos0], None, ws)
+        ref = ga.Layer(kinds[l], layers[l].k[0:1], layers[l].v[0:1])
+        b = ga.attn_verify(ref, q, kb, vb, [pos0], None, ws)
+        torch.cuda.synchronize()
+        diff = (a - b).abs().max().item()
+        if not diff < 0.05:
+            raise RuntimeError("fp8 verify of layer %d differs from bf16 by "
+                               "%g" % (l, diff))
+    flops = kvb = 0
+    for kind in kinds:
+        flops += pairs_block(kind, pos0, n) * 4 * ga.HQ * ga.D
+        keys = CTX if kind == ga.GLOBAL else min(CTX, 2048 + n - 1)
+        kvb += keys * FP8_TOKEN_BYTES
+    return {"ms_per_step": round(ms, 4),
+            "kv_GBps": round(kvb / (ms * 1e-3) / 1e9, 2),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "workload": "52-layer verify over fp8 caches, 16 drafted tokens "
+                        "at 131056..131071, batch 1"}
 
 
 def bench_verify(ga, torch, layers, kinds, B, reps=5, seed=4004):

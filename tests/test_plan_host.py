@@ -31,8 +31,9 @@ void shim_plan_decode(int kind, int B, long long keys, int cus, int xcds,
   out[3] = (long long)decode_ws_bytes(B, p);
 }
 void shim_plan_block(int kind, int B, int n, long long keys, int cus,
-                     int xcds, long long* out) {
-  const BlockPlan p = plan_block(kind, B, n, keys, DeviceShape{cus, xcds});
+                     int xcds, int always_split, long long* out) {
+  const BlockPlan p = plan_block(kind, B, n, keys, DeviceShape{cus, xcds},
+                                 always_split != 0);
   out[0] = p.qpw;
   out[1] = p.qgroups;
   out[2] = p.splits;
@@ -63,16 +64,18 @@ def plans(tmp_path_factory):
     lib = ctypes.CDLL(str(so))
     i, ll = ctypes.c_int, ctypes.c_longlong
     lib.shim_plan_decode.argtypes = [i, i, ll, i, i, ctypes.POINTER(ll)]
-    lib.shim_plan_block.argtypes = [i, i, i, ll, i, i, ctypes.POINTER(ll)]
+    lib.shim_plan_block.argtypes = [i, i, i, ll, i, i, i,
+                                    ctypes.POINTER(ll)]
 
     def decode(kind, B, keys, cus, xcds=8):
         out = (ll * 4)()
         lib.shim_plan_decode(kind, B, keys, cus, xcds, out)
         return dict(zip(("splits", "tps", "hpw", "ws"), out))
 
-    def block(kind, B, n, keys, cus, xcds=8):
+    def block(kind, B, n, keys, cus, xcds=8, always_split=False):
         out = (ll * 8)()
-        lib.shim_plan_block(kind, B, n, keys, cus, xcds, out)
+        lib.shim_plan_block(kind, B, n, keys, cus, xcds, int(always_split),
+                            out)
         return dict(zip(("qpw", "qgroups", "splits", "grid", "walks", "klin",
                          "part", "ws"), out))
     return decode, block
@@ -181,3 +184,28 @@ def test_block_plans_on_a_full_mi355x(plans):
     # prefill chunk of 4096: 512 work items walked by 256 workgroups
     pf = block(GLOBAL, 1, 4096, 131072, 256)
     assert (pf["splits"], pf["grid"], pf["walks"]) == (1, 256, 2)
+
+
+@pytest.mark.parametrize("cus,xcds", SHAPES)
+def test_block_plans_always_split(plans, cus, xcds):
+    """Calls over fp8 caches (verification, drafted blocks) always take the
+    key-split kernels: one or more splits, partials for every split, no
+    rotated-key copy, one work item per workgroup, and 8-token workgroups on
+    local layers."""
+    _, block = plans
+    for kind in (LOCAL, GLOBAL):
+        for B in (1, 4, 64):
+            for n, ctx in ((1, 1), (16, 16), (1, 100), (16, 2064),
+                           (16, 131072)):
+                keys = min(ctx, W) if kind == LOCAL else ctx
+                p = block(kind, B, n, keys, cus, xcds, always_split=True)
+                qpw = 8 if kind == LOCAL else 16
+                assert p["qpw"] == qpw
+                groups = -(-n // qpw) * 2 * B
+                wg_keys = W - 1 + qpw if kind == LOCAL else keys
+                assert 1 <= p["splits"] <= min(BLK_MAX_SPLITS,
+                                               -(-wg_keys // TILE))
+                assert p["walks"] == 1 and p["klin"] == 0
+                assert p["grid"] == p["splits"] * groups
+                assert p["part"] >= groups * p["splits"] * qpw * 16 * 272
+                assert p["ws"] >= p["part"]
