@@ -22,7 +22,7 @@ __all__ = [
     "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
     "attn_decode", "attn_decode_append", "attn_decode_dev",
     "attn_decode_noalloc", "LayerFp8", "kv_append_fp8", "attn_decode_fp8",
-    "attn_verify_fp8", "attn_draft_block_fp8", "workspace_bytes", "workspace", "status_string", "abi_version",
+    "attn_verify_fp8", "attn_draft_block_fp8", "attn_prefill_fp8", "workspace_bytes", "workspace", "status_string", "abi_version",
     "library_path", "layer_kind", "NUM_LAYERS",
 ]
 
@@ -112,7 +112,8 @@ def _load():
         lib.gqa_attn_decode_fp8.restype = i32
         lib.gqa_attn_decode_fp8.argtypes = [L8, p, p, i32, p, p,
                                             ctypes.c_size_t, p]
-        for name in ("gqa_attn_verify_fp8", "gqa_attn_draft_block_fp8"):
+        for name in ("gqa_attn_verify_fp8", "gqa_attn_draft_block_fp8",
+                     "gqa_attn_prefill_fp8"):
             f = getattr(lib, name)
             f.restype = i32
             f.argtypes = [L8, p, p, p, p, i32, i32, p, p, ctypes.c_size_t, p]
@@ -454,6 +455,17 @@ def attn_draft_block_fp8(layer: LayerFp8, q, k_blk, v_blk, pos0, out=None,
     return _block_common(_load().gqa_attn_draft_block_fp8,
                          "gqa_attn_draft_block_fp8", OP_DRAFT, torch.float32,
                          layer, q, k_blk, v_blk, pos0, out, ws, stream)
+
+
+def attn_prefill_fp8(layer: LayerFp8, q, k_chunk, v_chunk, pos0, out=None,
+                     ws=None, stream=None):
+    """:func:`attn_prefill` over an fp8 cache: the cached tokens are read as
+    their dequantised values, the chunk's own tokens at their bf16 values.
+    Returns bf16 [B, n, 32, 128]; append the chunk with
+    :func:`kv_append_fp8` afterwards."""
+    return _block_common(_load().gqa_attn_prefill_fp8, "gqa_attn_prefill_fp8",
+                         OP_PREFILL, torch.bfloat16, layer, q, k_chunk,
+                         v_chunk, pos0, out, ws, stream)
 
 
 def attn_draft_block(layer: Layer, q, k_blk, v_blk, pos0, out=None, ws=None,

@@ -82,11 +82,11 @@ size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx) {
       const int64_t keys = visible_keys(kind, max_ctx - 1);
       const DeviceShape dev = current_device_shape();
       const size_t need = block_ws_bytes(plan_block(kind, B, n, keys, dev));
-      if (!verify) return need;
-      // one verify workspace serves both cache formats (fp8 calls always
-      // split their keys)
-      const size_t need8 =
-          block_ws_bytes(plan_block(kind, B, n, keys, dev, true));
+      // one workspace serves both cache formats (fp8 calls plan their own
+      // way: verification always splits its keys, prefill never does)
+      const size_t need8 = block_ws_bytes(plan_block(
+          kind, B, n, keys, dev,
+          verify ? BlockFp8::kSplit : BlockFp8::kWalk));
       return need > need8 ? need : need8;
     }
     default:
@@ -332,19 +332,20 @@ int gqa_attn_draft_block(const gqa_layer* layer, const void* q,
                     true, true, stream);
 }
 
-// Verification or a drafted block over an fp8 cache.
+// Verification, a drafted block or a prefill chunk over an fp8 cache.
 static int block_impl_fp8(const gqa_layer_fp8* layer, const void* q,
                           const void* k_blk, const void* v_blk,
-                          const int64_t* pos0, int B, int n, float* out,
-                          void* ws, size_t ws_bytes, bool together,
-                          void* stream) {
+                          const int64_t* pos0, int B, int n, void* out,
+                          void* ws, size_t ws_bytes, bool verify,
+                          bool together, void* stream) {
   int64_t max_keys = 0;
-  int rc = check_block_fp8(layer, q, k_blk, v_blk, pos0, B, n, out,
+  int rc = check_block_fp8(layer, q, k_blk, v_blk, pos0, B, n, out, verify,
                            &max_keys);
   if (rc != GQA_OK) return rc;
   if (together && layer->kind != GQA_GLOBAL) return GQA_ERR_UNSUPPORTED;
   const BlockPlan plan =
-      plan_block(layer->kind, B, n, max_keys, current_device_shape(), true);
+      plan_block(layer->kind, B, n, max_keys, current_device_shape(),
+                 verify ? BlockFp8::kSplit : BlockFp8::kWalk);
   if (!ws) return GQA_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
   if (ws_bytes < block_ws_bytes(plan)) return GQA_ERR_WS_TOO_SMALL;
@@ -359,7 +360,7 @@ static int block_impl_fp8(const gqa_layer_fp8* layer, const void* q,
   p.v_scale = layer->v_scale;
   p.scale_stride = layer->scale_stride;
   p.capacity = layer->capacity;
-  p.part = reinterpret_cast<float*>(ws);
+  p.part = plan.part_bytes ? reinterpret_cast<float*>(ws) : nullptr;
   p.out = out;
   p.seq_stride = layer->seq_stride;  // bytes of codes per sequence
   p.n = n;
@@ -377,7 +378,7 @@ static int block_impl_fp8(const gqa_layer_fp8* layer, const void* q,
   }
   for (int b = 0; b < B; ++b) p.pos0[b] = pos0[b];
   hipError_t e =
-      launch_block(p, plan, local, true, B, (hipStream_t)stream, true);
+      launch_block(p, plan, local, verify, B, (hipStream_t)stream, true);
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
@@ -386,7 +387,7 @@ int gqa_attn_verify_fp8(const gqa_layer_fp8* layer, const void* q,
                         const int64_t* pos0, int B, int n, float* out,
                         void* ws, size_t ws_bytes, void* stream) {
   return block_impl_fp8(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
-                        false, stream);
+                        true, false, stream);
 }
 
 int gqa_attn_draft_block_fp8(const gqa_layer_fp8* layer, const void* q,
@@ -394,7 +395,15 @@ int gqa_attn_draft_block_fp8(const gqa_layer_fp8* layer, const void* q,
                              const int64_t* pos0, int B, int n, float* out,
                              void* ws, size_t ws_bytes, void* stream) {
   return block_impl_fp8(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
-                        true, stream);
+                        true, true, stream);
+}
+
+int gqa_attn_prefill_fp8(const gqa_layer_fp8* layer, const void* q,
+                         const void* k_chunk, const void* v_chunk,
+                         const int64_t* pos0, int B, int n, void* out,
+                         void* ws, size_t ws_bytes, void* stream) {
+  return block_impl_fp8(layer, q, k_chunk, v_chunk, pos0, B, n, out, ws,
+                        ws_bytes, false, false, stream);
 }
 
 int gqa_attn_prefill(const gqa_layer* layer, const void* q,

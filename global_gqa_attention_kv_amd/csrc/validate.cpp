@@ -159,9 +159,9 @@ int check_block(const gqa_layer* L, const void* q, const void* k_blk,
 
 int check_block_fp8(const gqa_layer_fp8* L, const void* q, const void* k_blk,
                     const void* v_blk, const int64_t* pos0, int B, int n,
-                    const void* out, int64_t* max_keys) {
+                    const void* out, bool verify, int64_t* max_keys) {
   if (!q || !k_blk || !v_blk || !pos0 || !out || B < 1 || B > GQA_MAX_BATCH ||
-      n < 1 || n > GQA_MAX_VERIFY)
+      n < 1 || n > (verify ? GQA_MAX_VERIFY : GQA_MAX_CONTEXT))
     return GQA_ERR_INVALID_ARG;
   int rc = check_layer_fp8(L);
   if (rc != GQA_OK) return rc;

@@ -30,9 +30,9 @@ int check_decode_fp8(const gqa_layer_fp8* L, const void* q, const int64_t* pos,
 int check_block(const gqa_layer* L, const void* q, const void* k_blk,
                 const void* v_blk, const int64_t* pos0, int B, int n,
                 const void* out, bool verify, int64_t* max_keys);
-// Verification (n <= 16) of a block over an fp8 cache.
+// The same over an fp8 cache.
 int check_block_fp8(const gqa_layer_fp8* L, const void* q, const void* k_blk,
                     const void* v_blk, const int64_t* pos0, int B, int n,
-                    const void* out, int64_t* max_keys);
+                    const void* out, bool verify, int64_t* max_keys);
 
 }  // namespace gqa

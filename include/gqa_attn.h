@@ -328,6 +328,22 @@ int gqa_attn_draft_block_fp8(const gqa_layer_fp8* layer, const void* q,
                              const int64_t* pos0, int B, int n, float* out,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* gqa_attn_prefill over an fp8 cache: a chunk of n (1..GQA_MAX_CONTEXT)
+ * prompt tokens per sequence at pos0[b] .. pos0[b]+n-1, attending causally
+ * (local layers: banded over 2048 positions, with RoPE) to the cached
+ * tokens as their dequantised values and to the chunk's own tokens at their
+ * bf16 values (k_chunk, v_chunk [B][n][2][128] bf16, not in the cache yet;
+ * append them with gqa_kv_append_fp8 afterwards).  q [B][n][32][128] bf16,
+ * out [B][n][32][128] bf16; workspace
+ * gqa_workspace_bytes(GQA_OP_PREFILL, kind, B, n, max pos0 + n) (one prefill
+ * workspace serves both cache formats); errors as gqa_attn_prefill.
+ * Pages: runtimewire.com "Long context still costs compute" and "Narrow
+ * cache". */
+int gqa_attn_prefill_fp8(const gqa_layer_fp8* layer, const void* q,
+                         const void* k_chunk, const void* v_chunk,
+                         const int64_t* pos0, int B, int n, void* out,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes an operation needs for any call on a layer of `kind` with
  * batch B, n tokens per sequence and context (keys visible to the last
  * query) at most max_ctx.  Returns 0 for invalid arguments. */

@@ -359,7 +359,8 @@ def test_fp8_decode_validation(lib):
 
 
 @pytest.mark.parametrize("fn", ["gqa_attn_verify_fp8",
-                                "gqa_attn_draft_block_fp8"])
+                                "gqa_attn_draft_block_fp8",
+                                "gqa_attn_prefill_fp8"])
 def test_fp8_block_validation(lib, fn):
     f = getattr(lib, fn)
     L = _layer8()
@@ -375,7 +376,11 @@ def test_fp8_block_validation(lib, fn):
     assert call(vb=None) == E_ARG
     assert call(out=None) == E_ARG
     assert call(n=0) == E_ARG
-    assert call(n=17) == E_ARG                          # block of at most 16
+    if fn != "gqa_attn_prefill_fp8":
+        assert call(n=17) == E_ARG                      # block of at most 16
+    else:
+        assert call(n=17, pos=_pos(0), ws_bytes=0) == E_WS
+        assert call(n=ga.MAX_CONTEXT + 1) == E_ARG
     assert call(B=0) == E_ARG
     assert call(ws=None) == E_ARG
     assert call(layer=_layer8(ks=0)) == E_ARG
@@ -385,11 +390,20 @@ def test_fp8_block_validation(lib, fn):
     assert call(ws=FAKE + 64) == E_ALN
     assert call(pos=_pos(4096 - 15)) == E_POS           # pos0 + n > capacity
     assert call(pos=_pos(-1)) == E_POS
-    op = ga.OP_VERIFY if fn == "gqa_attn_verify_fp8" else ga.OP_DRAFT
+    op = {"gqa_attn_verify_fp8": ga.OP_VERIFY,
+          "gqa_attn_draft_block_fp8": ga.OP_DRAFT,
+          "gqa_attn_prefill_fp8": ga.OP_PREFILL}[fn]
     need = ga.workspace_bytes(op, ga.GLOBAL, 1, 16, 4096)
-    assert call(pos=_pos(4080), ws_bytes=need - 1) == E_WS
+    if fn != "gqa_attn_prefill_fp8":
+        assert call(pos=_pos(4080), ws_bytes=need - 1) == E_WS
+    else:
+        # fp8 prefill keeps no partial sums; the query covers the bf16 call's
+        assert call(pos=_pos(4080), ws_bytes=255) == E_WS
     if fn == "gqa_attn_draft_block_fp8":
         assert call(layer=_layer8(kind=ga.LOCAL)) == E_UNS
+    elif fn == "gqa_attn_prefill_fp8":
+        assert call(layer=_layer8(kind=ga.LOCAL), pos=_pos(4080),
+                    ws_bytes=255) == E_WS
     else:
         # the local workspace query covers the fp8 call's key splits
         need = ga.workspace_bytes(op, ga.LOCAL, 1, 16, 4096)

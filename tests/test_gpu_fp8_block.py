@@ -7,7 +7,8 @@ from the oracle's own quantisation of the same bf16 stream
 values, the block's own tokens (which arrive with the call, not yet in the
 cache) at their bf16 values.  Bar: max abs <= 2e-2, mean abs <= 2e-3, and the
 max/RMS gate beyond 32K keys.  Covered: both layer kinds, blocks of 1, 5 and
-16 tokens, ragged batches (an empty prior, a prior shorter than a tile, a
+16 tokens, prefill chunks (every row of chunks up to 2500 tokens, sampled
+and edge rows of the last 4096-token chunk of 131072), ragged batches (an empty prior, a prior shorter than a tile, a
 local window that wraps the ring), the full 131056-token prior, needles at
 key-split and tile edges and inside the block, the drafted block predicted
 together, and an exactly held cache against the bf16 verification."""
@@ -50,11 +51,13 @@ def _fill_prior(kind, streams, pos0, capacity):
 
 
 def _run(kind, pos0, n, seed, together=False, capacity=None, streams=None,
-         q=None):
+         q=None, prefill=False, rows=None):
+    """The library's call and the oracle's values; rows: the query tokens
+    the oracle computes (all by default)."""
     B = len(pos0)
     print("fp8 %s kind=%d B=%d n=%d pos0=%s" %
-          ("draft" if together else "verify", kind, B, n, pos0[:4]),
-          flush=True)
+          ("prefill" if prefill else "draft" if together else "verify",
+           kind, B, n, pos0[:4]), flush=True)
     if streams is None:
         streams = [si.stream(si.seq_seed(seed, b), pos0[b] + n)
                    for b in range(B)]
@@ -68,20 +71,22 @@ def _run(kind, pos0, n, seed, together=False, capacity=None, streams=None,
     layer, prior = _fill_prior(kind, streams, pos0, capacity)
     kb = torch.stack([streams[b][0][pos0[b]:pos0[b] + n] for b in range(B)])
     vb = torch.stack([streams[b][1][pos0[b]:pos0[b] + n] for b in range(B)])
-    fn = ga.attn_draft_block_fp8 if together else ga.attn_verify_fp8
+    fn = (ga.attn_prefill_fp8 if prefill else
+          ga.attn_draft_block_fp8 if together else ga.attn_verify_fp8)
     got = fn(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
     torch.cuda.synchronize()
+    rows = np.arange(n) if rows is None else np.asarray(rows)
     want = []
     for b in range(B):
         lo, kc, ks, vc, vs = prior[b]
-        qpos = (np.full(n, pos0[b] + n - 1) if together
-                else pos0[b] + np.arange(n))
+        qpos = (np.full(len(rows), pos0[b] + n - 1) if together
+                else pos0[b] + rows)
         want.append(fp8.attend_mixed(
-            si.bits(q[b]), qpos, kc, ks, vc, vs, si.bits(kb[b]),
+            si.bits(q[b][rows]), qpos, kc, ks, vc, vs, si.bits(kb[b]),
             si.bits(vb[b]), lo, hq=ga.HQ, hkv=ga.HKV, d=ga.D,
             window=ga.WINDOW if kind == ga.LOCAL else 0,
             rope=kind == ga.LOCAL, theta=10000.0))
-    return got.cpu().numpy(), np.stack(want), prior
+    return got.float().cpu().numpy()[:, rows], np.stack(want), prior
 
 
 @pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
@@ -158,3 +163,30 @@ def test_verify_fp8_exact_cache_matches_bf16_verify(kind):
     torch.cuda.synchronize()
     check_close(got8, want, "verify fp8 exact cache kind=%d" % kind)
     check_close(got8, got16.cpu().numpy(), "fp8 vs bf16 verify kind=%d" % kind)
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+@pytest.mark.parametrize("pos0,n", [([0, 3000], 300), ([37, 2100], 129),
+                                    ([5000], 2500)])
+def test_prefill_fp8_every_row(kind, pos0, n):
+    """Chunks over the fp8 cache against the oracle, every row (bf16 out):
+    an empty prior, a local window across the ring's end, a chunk longer
+    than the window."""
+    got, want, _ = _run(kind, pos0, n, 8251 + n, prefill=True)
+    check_close(got, want, "prefill fp8 kind=%d n=%d" % (kind, n))
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_prefill_fp8_last_chunk_131072_sampled(kind):
+    """The last 4096-token chunk of a 131072-token prompt over the fp8
+    cache: 256 sampled rows plus the chunk's edge rows."""
+    n, pos0 = 4096, ga.MAX_CONTEXT - 4096
+    rng = np.random.default_rng(8261)
+    rows = np.unique(np.concatenate([
+        rng.choice(n, 256, replace=False),
+        [0, 1, 15, 16, 63, 64, 2046, 2047, 2048, 4094, 4095]]))
+    got, want, _ = _run(kind, [pos0], n, 8261, prefill=True, rows=rows,
+                        capacity=ga.MAX_CONTEXT if kind == ga.GLOBAL
+                        else None)
+    check_close(got, want, "prefill fp8 131072 kind=%d" % kind,
+                ctx=ga.MAX_CONTEXT if kind == ga.GLOBAL else ga.WINDOW)
