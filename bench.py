@@ -440,15 +440,20 @@ def bench_draft(ga, torch, layers, kinds, B, n_drafter=5, reps=5, seed=4404):
                         "context, batch %d" % (len(glob), B)}
 
 
-def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005):
+def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005,
+                  fp8=False):
     """Chunked causal prefill of `total` tokens in `chunk`-token chunks on
-    one local and one global layer: prefill then append per chunk."""
+    one local and one global layer: prefill then append per chunk (fp8:
+    over fp8 caches, appending with the quantiser)."""
     dev = torch.device("cuda")
     res = {}
     for kind in (ga.LOCAL, ga.GLOBAL):
         gen = torch.Generator(device=dev)
         gen.manual_seed(seed + kind)
-        layer = ga.Layer.allocate(kind, 1, device=dev)
+        layer = (ga.LayerFp8 if fp8 else ga.Layer).allocate(kind, 1,
+                                                              device=dev)
+        attend = ga.attn_prefill_fp8 if fp8 else ga.attn_prefill
+        append = ga.kv_append_fp8 if fp8 else ga.kv_append
         q = torch.randn((1, total, ga.HQ, ga.D), generator=gen, device=dev).to(torch.bfloat16)
         k = torch.randn((1, total, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((1, total, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
@@ -459,8 +464,8 @@ def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005):
         def run():
             for c0 in range(0, total, chunk):
                 sl = slice(c0, c0 + chunk)
-                ga.attn_prefill(layer, q[:, sl], k[:, sl], v[:, sl], [c0], out, ws)
-                ga.kv_append(layer, k[:, sl], v[:, sl], [c0])
+                attend(layer, q[:, sl], k[:, sl], v[:, sl], [c0], out, ws)
+                append(layer, k[:, sl], v[:, sl], [c0])
 
         run()
         torch.cuda.synchronize()
@@ -482,7 +487,10 @@ def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005):
         del q, k, v, layer, ws, out
         torch.cuda.empty_cache()
     res["workload"] = ("prefill of %d tokens in %d-token chunks (prefill + "
-                       "append per chunk), batch 1" % (total, chunk))
+                       "append per chunk), batch 1%s" %
+                       (total, chunk, ", over fp8 caches" if fp8 else ""))
+    if not fp8:
+        res["fp8"] = bench_prefill(ga, torch, chunk, total, reps, seed, True)
     return res
 
 
