@@ -457,7 +457,8 @@ def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005,
         q = torch.randn((1, total, ga.HQ, ga.D), generator=gen, device=dev).to(torch.bfloat16)
         k = torch.randn((1, total, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((1, total, ga.HKV, ga.D), generator=gen, device=dev).to(torch.bfloat16)
-        ws = torch.empty(ga.workspace_bytes(ga.OP_PREFILL, kind, 1, chunk, total),
+        op = ga.OP_PREFILL_FP8 if fp8 else ga.OP_PREFILL
+        ws = torch.empty(ga.workspace_bytes(op, kind, 1, chunk, total),
                          dtype=torch.uint8, device=dev)
         out = torch.empty((1, chunk, ga.HQ, ga.D), dtype=torch.bfloat16, device=dev)
 

@@ -18,6 +18,7 @@ import torch
 
 __all__ = [
     "LOCAL", "GLOBAL", "OP_DECODE", "OP_VERIFY", "OP_PREFILL", "OP_DRAFT",
+    "OP_PREFILL_FP8",
     "MAX_VERIFY", "attn_verify", "attn_draft_block", "attn_prefill", "HQ", "HKV", "D", "WINDOW", "MAX_CONTEXT",
     "MAX_BATCH", "GqaError", "LibraryMissing", "Layer", "kv_append",
     "attn_decode", "attn_decode_append", "attn_decode_dev",
@@ -30,7 +31,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libgqa_attn.so")
 
 LOCAL, GLOBAL = 0, 1
-OP_DECODE, OP_VERIFY, OP_PREFILL, OP_DRAFT = 0, 1, 2, 3
+OP_DECODE, OP_VERIFY, OP_PREFILL, OP_DRAFT, OP_PREFILL_FP8 = 0, 1, 2, 3, 4
 MAX_VERIFY = 16
 HQ, HKV, D, WINDOW, MAX_CONTEXT, MAX_BATCH = 32, 2, 128, 2048, 131072, 64
 NUM_LAYERS = 52
@@ -464,7 +465,7 @@ def attn_prefill_fp8(layer: LayerFp8, q, k_chunk, v_chunk, pos0, out=None,
     Returns bf16 [B, n, 32, 128]; append the chunk with
     :func:`kv_append_fp8` afterwards."""
     return _block_common(_load().gqa_attn_prefill_fp8, "gqa_attn_prefill_fp8",
-                         OP_PREFILL, torch.bfloat16, layer, q, k_chunk,
+                         OP_PREFILL_FP8, torch.bfloat16, layer, q, k_chunk,
                          v_chunk, pos0, out, ws, stream)
 
 

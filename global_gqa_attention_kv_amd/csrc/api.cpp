@@ -38,6 +38,32 @@ DeviceShape current_device_shape() {
 
 }  // namespace gqa
 
+namespace gqa {
+
+// Workspace of a prefill chunk over an fp8 cache: the bf16 prefill's own
+// workspace, then a bf16 copy of the prior (K then V, copy_rows tokens per
+// sequence: the positions before the chunk on global layers, the ring on
+// local layers).
+struct PrefillFp8Ws {
+  BlockPlan plan;
+  size_t block_bytes;   // the bf16 prefill's workspace
+  size_t copy_off;      // byte offset of the K copy
+  int64_t copy_rows;
+  size_t total;
+};
+static PrefillFp8Ws prefill_fp8_ws(int kind, int B, int n, int64_t max_keys,
+                                   int64_t max_ctx, const DeviceShape& dev) {
+  PrefillFp8Ws w;
+  w.plan = plan_block(kind, B, n, max_keys, dev);
+  w.block_bytes = block_ws_bytes(w.plan);
+  w.copy_off = (w.block_bytes + 255) & ~(size_t)255;
+  w.copy_rows = kind == GQA_LOCAL ? kW : (max_ctx > 1 ? max_ctx - 1 : 1);
+  w.total = w.copy_off + 2 * (size_t)B * w.copy_rows * kTokenElems * 2;
+  return w;
+}
+
+}  // namespace gqa
+
 using namespace gqa;
 
 extern "C" {
@@ -82,12 +108,18 @@ size_t gqa_workspace_bytes(int op, int kind, int B, int n, int64_t max_ctx) {
       const int64_t keys = visible_keys(kind, max_ctx - 1);
       const DeviceShape dev = current_device_shape();
       const size_t need = block_ws_bytes(plan_block(kind, B, n, keys, dev));
-      // one workspace serves both cache formats (fp8 calls plan their own
-      // way: verification always splits its keys, prefill never does)
-      const size_t need8 = block_ws_bytes(plan_block(
-          kind, B, n, keys, dev,
-          verify ? BlockFp8::kSplit : BlockFp8::kWalk));
+      if (!verify) return need;
+      // one verify workspace serves both cache formats (fp8 calls always
+      // split their keys)
+      const size_t need8 =
+          block_ws_bytes(plan_block(kind, B, n, keys, dev, true));
       return need > need8 ? need : need8;
+    }
+    case GQA_OP_PREFILL_FP8: {
+      if (n > GQA_MAX_CONTEXT) return 0;
+      const int64_t keys = visible_keys(kind, max_ctx - 1);
+      return prefill_fp8_ws(kind, B, n, keys, max_ctx,
+                            current_device_shape()).total;
     }
     default:
       return 0;
@@ -269,18 +301,14 @@ int gqa_attn_decode_noalloc(const gqa_layer* layer, const void* q,
                      nullptr, 0, true);
 }
 
-static int block_impl(const gqa_layer* layer, const void* q,
-                      const void* k_blk, const void* v_blk,
-                      const int64_t* pos0, int B, int n, void* out, void* ws,
-                      size_t ws_bytes, bool verify, bool together,
-                      void* stream) {
-  int64_t max_keys = 0;
-  int rc = check_block(layer, q, k_blk, v_blk, pos0, B, n, out, verify,
-                       &max_keys);
-  if (rc != GQA_OK) return rc;
-  if (together && layer->kind != GQA_GLOBAL) return GQA_ERR_UNSUPPORTED;
-  const BlockPlan plan =
-      plan_block(layer->kind, B, n, max_keys, current_device_shape());
+// A validated block call on a bf16 cache with its plan.
+static int block_launch(const gqa_layer* layer, const void* q,
+                        const void* k_blk, const void* v_blk,
+                        const int64_t* pos0, int B, int n, void* out,
+                        void* ws, size_t ws_bytes, bool verify, bool together,
+                        int64_t max_keys, const BlockPlan& plan,
+                        void* stream) {
+  (void)max_keys;
   if (!ws) return GQA_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
   if (ws_bytes < block_ws_bytes(plan)) return GQA_ERR_WS_TOO_SMALL;
@@ -317,6 +345,22 @@ static int block_impl(const gqa_layer* layer, const void* q,
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
+static int block_impl(const gqa_layer* layer, const void* q,
+                      const void* k_blk, const void* v_blk,
+                      const int64_t* pos0, int B, int n, void* out, void* ws,
+                      size_t ws_bytes, bool verify, bool together,
+                      void* stream) {
+  int64_t max_keys = 0;
+  int rc = check_block(layer, q, k_blk, v_blk, pos0, B, n, out, verify,
+                       &max_keys);
+  if (rc != GQA_OK) return rc;
+  if (together && layer->kind != GQA_GLOBAL) return GQA_ERR_UNSUPPORTED;
+  const BlockPlan plan =
+      plan_block(layer->kind, B, n, max_keys, current_device_shape());
+  return block_launch(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
+                      verify, together, max_keys, plan, stream);
+}
+
 int gqa_attn_verify(const gqa_layer* layer, const void* q, const void* k_blk,
                     const void* v_blk, const int64_t* pos0, int B, int n,
                     float* out, void* ws, size_t ws_bytes, void* stream) {
@@ -332,20 +376,19 @@ int gqa_attn_draft_block(const gqa_layer* layer, const void* q,
                     true, true, stream);
 }
 
-// Verification, a drafted block or a prefill chunk over an fp8 cache.
+// Verification or a drafted block over an fp8 cache.
 static int block_impl_fp8(const gqa_layer_fp8* layer, const void* q,
                           const void* k_blk, const void* v_blk,
                           const int64_t* pos0, int B, int n, void* out,
-                          void* ws, size_t ws_bytes, bool verify,
-                          bool together, void* stream) {
+                          void* ws, size_t ws_bytes, bool together,
+                          void* stream) {
   int64_t max_keys = 0;
-  int rc = check_block_fp8(layer, q, k_blk, v_blk, pos0, B, n, out, verify,
+  int rc = check_block_fp8(layer, q, k_blk, v_blk, pos0, B, n, out, true,
                            &max_keys);
   if (rc != GQA_OK) return rc;
   if (together && layer->kind != GQA_GLOBAL) return GQA_ERR_UNSUPPORTED;
   const BlockPlan plan =
-      plan_block(layer->kind, B, n, max_keys, current_device_shape(),
-                 verify ? BlockFp8::kSplit : BlockFp8::kWalk);
+      plan_block(layer->kind, B, n, max_keys, current_device_shape(), true);
   if (!ws) return GQA_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
   if (ws_bytes < block_ws_bytes(plan)) return GQA_ERR_WS_TOO_SMALL;
@@ -360,7 +403,7 @@ static int block_impl_fp8(const gqa_layer_fp8* layer, const void* q,
   p.v_scale = layer->v_scale;
   p.scale_stride = layer->scale_stride;
   p.capacity = layer->capacity;
-  p.part = plan.part_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  p.part = reinterpret_cast<float*>(ws);
   p.out = out;
   p.seq_stride = layer->seq_stride;  // bytes of codes per sequence
   p.n = n;
@@ -378,7 +421,7 @@ static int block_impl_fp8(const gqa_layer_fp8* layer, const void* q,
   }
   for (int b = 0; b < B; ++b) p.pos0[b] = pos0[b];
   hipError_t e =
-      launch_block(p, plan, local, verify, B, (hipStream_t)stream, true);
+      launch_block(p, plan, local, true, B, (hipStream_t)stream, true);
   return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
@@ -387,7 +430,7 @@ int gqa_attn_verify_fp8(const gqa_layer_fp8* layer, const void* q,
                         const int64_t* pos0, int B, int n, float* out,
                         void* ws, size_t ws_bytes, void* stream) {
   return block_impl_fp8(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
-                        true, false, stream);
+                        false, stream);
 }
 
 int gqa_attn_draft_block_fp8(const gqa_layer_fp8* layer, const void* q,
@@ -395,15 +438,62 @@ int gqa_attn_draft_block_fp8(const gqa_layer_fp8* layer, const void* q,
                              const int64_t* pos0, int B, int n, float* out,
                              void* ws, size_t ws_bytes, void* stream) {
   return block_impl_fp8(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
-                        true, true, stream);
+                        true, stream);
 }
 
 int gqa_attn_prefill_fp8(const gqa_layer_fp8* layer, const void* q,
                          const void* k_chunk, const void* v_chunk,
                          const int64_t* pos0, int B, int n, void* out,
                          void* ws, size_t ws_bytes, void* stream) {
-  return block_impl_fp8(layer, q, k_chunk, v_chunk, pos0, B, n, out, ws,
-                        ws_bytes, false, false, stream);
+  int64_t max_keys = 0;
+  int rc = check_block_fp8(layer, q, k_chunk, v_chunk, pos0, B, n, out, false,
+                           &max_keys);
+  if (rc != GQA_OK) return rc;
+  const bool local = layer->kind == GQA_LOCAL;
+  int64_t max_pos0 = 0;
+  for (int b = 0; b < B; ++b) max_pos0 = pos0[b] > max_pos0 ? pos0[b] : max_pos0;
+  const PrefillFp8Ws lay = prefill_fp8_ws(layer->kind, B, n, max_keys,
+                                          max_pos0 + n, current_device_shape());
+  if (!ws) return GQA_ERR_INVALID_ARG;
+  if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
+  if (ws_bytes < lay.total) return GQA_ERR_WS_TOO_SMALL;
+  char* const scratch = static_cast<char*>(ws);
+  // the prior of every sequence as bf16: global layers its positions
+  // 0 .. pos0 - 1 (slot = position), local layers the ring's slots that hold
+  // positions before pos0
+  DequantParams d;
+  memset(&d, 0, sizeof d);
+  d.k8 = static_cast<const uint8_t*>(layer->k);
+  d.v8 = static_cast<const uint8_t*>(layer->v);
+  d.k_scale = layer->k_scale;
+  d.v_scale = layer->v_scale;
+  d.seq_stride = layer->seq_stride;
+  d.scale_stride = layer->scale_stride;
+  d.capacity = layer->capacity;
+  d.k_out = reinterpret_cast<uint16_t*>(scratch + lay.copy_off);
+  d.v_out = d.k_out + (size_t)B * lay.copy_rows * kTokenElems;
+  d.out_stride = lay.copy_rows * kTokenElems;
+  int64_t max_rows = 0;
+  for (int b = 0; b < B; ++b) {
+    d.rows[b] = local ? (pos0[b] < kW ? pos0[b] : kW) : pos0[b];
+    if (d.rows[b] > max_rows) max_rows = d.rows[b];
+  }
+  hipError_t e = launch_dequant_cache(d, B, max_rows, (hipStream_t)stream);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  // the bf16 prefill over the copy, which holds the prior exactly where a
+  // bf16 cache of capacity copy_rows would
+  gqa_layer view;
+  memset(&view, 0, sizeof view);
+  view.kind = layer->kind;
+  view.window = layer->window;
+  view.capacity = lay.copy_rows;
+  view.rope_theta = layer->rope_theta;
+  view.k = d.k_out;
+  view.v = d.v_out;
+  view.seq_stride = d.out_stride;
+  return block_launch(&view, q, k_chunk, v_chunk, pos0, B, n, out, ws,
+                      lay.block_bytes, false, false, max_keys, lay.plan,
+                      stream);
 }
 
 int gqa_attn_prefill(const gqa_layer* layer, const void* q,

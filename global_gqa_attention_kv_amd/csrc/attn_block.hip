@@ -263,6 +263,7 @@ __device__ __forceinline__ float max16(const f32x16_t& v) {
 template <int QPW, bool LOCAL, bool SPLIT, bool OUT_F32, bool F8 = false>
 __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
     const BlockParams p) {
+  static_assert(!F8 || SPLIT, "fp8 caches: key-split calls only");
   constexpr F8Lds L8 = f8_lds(QPW / 2, QPW, LOCAL);
   constexpr int WAVES = QPW / 2;  // waves of 32 rows (2 tokens x 16 heads)
   constexpr int RING = kRing;
@@ -525,19 +526,11 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
       const bool blk = j >= pos0;
       static_for<0, 2>([&](auto IV) {
         u32x4_t lo, hi;
-        if (blk && p.n <= kF8BlkRows) {
+        if (blk) {
           const uint32_t src = lds_base + L8.blk +
                                (IV * kF8BlkRows + (j - pos0)) * 256 + cch * 32;
           lo = *reinterpret_cast<const lds_u32x4_t*>(src);
           hi = *reinterpret_cast<const lds_u32x4_t*>(src + 16);
-        } else if (blk) {
-          // a longer block (a prefill chunk): the row from the call's buffer
-          const uint4* src = reinterpret_cast<const uint4*>(
-              (IV ? p.v_blk : p.k_blk) +
-              ((int64_t)b * p.n + (j - pos0)) * kTokenElems + g * kD +
-              cch * 16);
-          lo = __builtin_bit_cast(u32x4_t, src[0]);
-          hi = __builtin_bit_cast(u32x4_t, src[1]);
         } else {
           const u32x4_t c = *reinterpret_cast<const lds_u32x4_t*>(
               lds_base + kF8Codes + SLOT * kCodeSlotB + IV * kCodeTileB +
@@ -869,11 +862,10 @@ __global__ __launch_bounds__(QPW * 32, 1) void block_attn_kernel(
   };
 
   if constexpr (F8) {
-    // a block of at most 16 tokens (verification): its bf16 K and V rows of
-    // this KV head (rows n .. 15 repeat the last), 8 KB, then the first code
-    // tiles; the block rows are waited for and published before any wave
-    // dequantises.  Longer blocks are read row by row when dequantised.
-    if (p.n <= kF8BlkRows) static_for<0, 8 / WAVES>([&](auto I) {
+    // the block's bf16 K and V rows of this KV head (rows n .. 15 repeat
+    // the last), 8 KB, then the first code tiles; the block rows are
+    // waited for and published before any wave dequantises
+    static_for<0, 8 / WAVES>([&](auto I) {
       const int u = (I * WAVES + w) * 64 + lane;  // 16-byte chunk of the 8 KB
       const int rr = u >> 4, ch = u & 15;         // K rows 0..15, V 16..31
       const int tok = min(rr & 15, p.n - 1);
@@ -1127,53 +1119,38 @@ hipError_t launch_main(const BlockParams& p, const BlockPlan& plan, int B,
 
 }  // namespace
 
-// fp8 caches.  Verification and drafted blocks (fp32 out): the key-split
-// kernels for any split count, then the merge; local layers take 8-token
-// workgroups, global layers 16.  Prefill (bf16 out): no key splits, each
-// 8-token workgroup walking its items.
+// fp8 caches (verification and drafted blocks): the key-split kernels for
+// any split count, then the merge.  Local layers take 8-token workgroups,
+// global layers 16.
 static hipError_t launch_block_fp8(const BlockParams& p, const BlockPlan& plan,
-                                   bool local, bool out_f32, int B,
-                                   hipStream_t s) {
-  const dim3 grid(plan.grid);
-  const int qpw = out_f32 && !local ? kBlkQpw : kBlkQpwSmall;
-  if (p.qpw != plan.qpw || plan.qpw != qpw || plan.klin_bytes != 0 ||
-      plan.grid < 1)
+                                   bool local, int B, hipStream_t s) {
+  if (plan.walks != 1 || plan.klin_bytes != 0 || p.part == nullptr ||
+      p.n > kF8BlkRows || p.splits > kBlkMaxSplits ||
+      plan.grid != p.splits * p.qgroups * kHkv * B || p.qpw != plan.qpw ||
+      plan.qpw != (local ? kBlkQpwSmall : kBlkQpw))
     return hipErrorInvalidValue;
-  if (out_f32) {
-    if (plan.walks != 1 || p.part == nullptr || p.n > kF8BlkRows ||
-        p.splits > kBlkMaxSplits ||
-        plan.grid != p.splits * p.qgroups * kHkv * B)
-      return hipErrorInvalidValue;
-    if (local)
-      hipLaunchKernelGGL(
-          (block_attn_kernel<kBlkQpwSmall, true, true, true, true>), grid,
-          dim3(kBlkQpwSmall * 32), 0, s, p);
-    else
-      hipLaunchKernelGGL(
-          (block_attn_kernel<kBlkQpw, false, true, true, true>), grid,
-          dim3(kBlkQpw * 32), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((block_merge_kernel<true>), dim3(B * p.n * kHq),
-                       dim3(64), 0, s, p);
-    return hipGetLastError();
-  }
-  if (p.splits != 1) return hipErrorInvalidValue;
+  const dim3 grid(plan.grid);
   if (local)
     hipLaunchKernelGGL(
-        (block_attn_kernel<kBlkQpwSmall, true, false, false, true>), grid,
+        (block_attn_kernel<kBlkQpwSmall, true, true, true, true>), grid,
         dim3(kBlkQpwSmall * 32), 0, s, p);
   else
-    hipLaunchKernelGGL(
-        (block_attn_kernel<kBlkQpwSmall, false, false, false, true>), grid,
-        dim3(kBlkQpwSmall * 32), 0, s, p);
+    hipLaunchKernelGGL((block_attn_kernel<kBlkQpw, false, true, true, true>),
+                       grid, dim3(kBlkQpw * 32), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((block_merge_kernel<true>), dim3(B * p.n * kHq), dim3(64),
+                     0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_block(const BlockParams& p, const BlockPlan& plan,
                         bool local, bool out_f32, int B, hipStream_t s,
                         bool fp8) {
-  if (fp8) return launch_block_fp8(p, plan, local, out_f32, B, s);
+  if (fp8) {
+    if (!out_f32) return hipErrorInvalidValue;
+    return launch_block_fp8(p, plan, local, B, s);
+  }
   // 8-token workgroups only for local layers with key splits
   const bool small = local && p.splits > 1 && plan.qpw == kBlkQpwSmall;
   if ((plan.qpw != kBlkQpw && !small) || p.qpw != plan.qpw ||

@@ -48,6 +48,25 @@ struct AppendFp8Params {
 hipError_t launch_kv_append_fp8(const AppendFp8Params& p, int B, int count,
                                 hipStream_t s);
 
+// The first rows[b] slots of each sequence's fp8 cache as bf16 (code x
+// scale, rounded once to bf16), into a copy the bf16 block kernels read:
+// the prior a prefill chunk over an fp8 cache attends to (kv_append.hip).
+struct DequantParams {
+  const uint8_t* k8;       // codes, sequence b at byte b * seq_stride
+  const uint8_t* v8;
+  const float* k_scale;    // scales [B][2][capacity]
+  const float* v_scale;
+  uint16_t* k_out;         // bf16 copy, sequence b at element b * out_stride
+  uint16_t* v_out;
+  int64_t seq_stride;
+  int64_t scale_stride;
+  int64_t capacity;
+  int64_t out_stride;
+  int64_t rows[kMaxBatch];
+};
+hipError_t launch_dequant_cache(const DequantParams& p, int B,
+                                int64_t max_rows, hipStream_t s);
+
 // ---------------------------------------------------------------- decode
 // Global-layer decode: waves per workgroup (each takes 16 keys of every
 // tile for all 16 query heads) and K and V tile slots in its LDS ring (16 KB

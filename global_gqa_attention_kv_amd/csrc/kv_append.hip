@@ -93,4 +93,50 @@ hipError_t launch_kv_append_fp8(const AppendFp8Params& p, int B, int count,
   return hipGetLastError();
 }
 
+// fp8 cache -> bf16 copy for a prefill chunk over an fp8 cache: 32 threads
+// per slot, thread c of K (c < 16) or V takes the 16 codes 16 (c % 8) .. of
+// KV head c / 8.  Each code becomes its exact bf16 value, is multiplied by
+// its row's scale in fp32 and rounded once to bf16 (the operand rounding the
+// bf16 kernels apply to every key they rotate or scale).
+__global__ __launch_bounds__(256) void dequant_cache_kernel(
+    const DequantParams p) {
+  const int b = blockIdx.y;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t slot = idx >> 5;
+  if (slot >= p.rows[b]) return;
+  const int part = (int)(idx & 31);
+  const bool is_v = part >= 16;
+  const int c = part & 15, g = c >> 3;
+  const uint8_t* src = (is_v ? p.v8 : p.k8) + (int64_t)b * p.seq_stride +
+                       slot * kTokenElems + c * 16;
+  const float sc = (is_v ? p.v_scale : p.k_scale)[(int64_t)b * p.scale_stride +
+                                                 g * p.capacity + slot];
+  const uint4 raw = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false));
+    const uint32_t hi = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true));
+    o[2 * e] = pack_bf16(bf16_lo(lo) * sc, bf16_hi(lo) * sc);
+    o[2 * e + 1] = pack_bf16(bf16_lo(hi) * sc, bf16_hi(hi) * sc);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(
+      (is_v ? p.v_out : p.k_out) + (int64_t)b * p.out_stride +
+      slot * kTokenElems + c * 16);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+hipError_t launch_dequant_cache(const DequantParams& p, int B,
+                                int64_t max_rows, hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_cache_kernel,
+                     dim3((unsigned)((max_rows * 32 + 255) / 256), B),
+                     dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace gqa

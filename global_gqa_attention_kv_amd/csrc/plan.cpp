@@ -55,8 +55,7 @@ size_t decode_ws_bytes(int B, const DecodePlan& plan) {
 // two tiles, its chain of query load, tile rotation, products and partial
 // rows is latency, and half the rows shorten it.
 BlockPlan plan_block(int kind, int B, int n, int64_t max_keys,
-                     const DeviceShape& dev, BlockFp8 fp8) {
-  const bool always_split = fp8 == BlockFp8::kSplit;
+                     const DeviceShape& dev, bool always_split) {
   const int cus = cus_of(dev);
   BlockPlan p;
   auto shape = [&](int qpw) {
@@ -78,21 +77,18 @@ BlockPlan plan_block(int kind, int B, int n, int64_t max_keys,
     return groups;
   };
   int64_t groups = shape(kBlkQpw);
-  if (fp8 == BlockFp8::kWalk) {
-    groups = shape(kBlkQpwSmall);
-  } else if (kind == GQA_LOCAL && (p.splits > 1 || always_split)) {
+  if (kind == GQA_LOCAL && (p.splits > 1 || always_split)) {
     groups = shape(kBlkQpwSmall);
     // groups of 8 fill the CUs (split calls over fp8 caches keep them)
     if (p.splits == 1 && !always_split) groups = shape(kBlkQpw);
   }
-  if (fp8 == BlockFp8::kWalk) p.splits = 1;
   const bool split = p.splits > 1 || always_split;
   const int64_t items = (int64_t)p.splits * groups;
   p.walks = split ? 1 : (int)((items + cus - 1) / cus);
   p.grid = (int)((items + p.walks - 1) / p.walks);
   // local layers without key splits read pre-rotated keys from the
   // workspace; split calls rotate each tile in LDS
-  p.klin_bytes = kind == GQA_LOCAL && !split && fp8 == BlockFp8::kNo
+  p.klin_bytes = kind == GQA_LOCAL && !split
                      ? align256((size_t)B * ((size_t)kW + n) * kTokenElems * 2)
                      : 0;
   p.part_bytes = split

@@ -73,13 +73,11 @@ struct BlockPlan {
   size_t klin_bytes;   // local: pre-rotated keys
   size_t part_bytes;   // split partials
 };
-// Calls over fp8 caches: verification and drafted blocks always take key
-// splits (one or more, partials and merge), with 8-token workgroups on
-// local layers; prefill never splits and takes 8-token workgroups on both
-// kinds (the 16-token instances spill); neither uses a rotated-key copy.
-enum class BlockFp8 { kNo, kSplit, kWalk };
+// always_split: key splits (one or more, partials and merge) whatever the
+// shape, with 8-token workgroups on local layers, as verification and
+// drafted blocks over fp8 caches take.
 BlockPlan plan_block(int kind, int B, int n, int64_t max_keys,
-                     const DeviceShape& dev, BlockFp8 fp8 = BlockFp8::kNo);
+                     const DeviceShape& dev, bool always_split = false);
 size_t block_ws_bytes(const BlockPlan& plan);
 
 }  // namespace gqa

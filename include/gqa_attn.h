@@ -75,6 +75,7 @@ extern "C" {
 #define GQA_OP_VERIFY 1
 #define GQA_OP_PREFILL 2
 #define GQA_OP_DRAFT 3
+#define GQA_OP_PREFILL_FP8 4  /* gqa_attn_prefill_fp8 */
 
 /* Status codes. */
 #define GQA_OK 0
@@ -334,9 +335,12 @@ int gqa_attn_draft_block_fp8(const gqa_layer_fp8* layer, const void* q,
  * tokens as their dequantised values and to the chunk's own tokens at their
  * bf16 values (k_chunk, v_chunk [B][n][2][128] bf16, not in the cache yet;
  * append them with gqa_kv_append_fp8 afterwards).  q [B][n][32][128] bf16,
- * out [B][n][32][128] bf16; workspace
- * gqa_workspace_bytes(GQA_OP_PREFILL, kind, B, n, max pos0 + n) (one prefill
- * workspace serves both cache formats); errors as gqa_attn_prefill.
+ * out [B][n][32][128] bf16.  The call first writes a bf16 copy of the
+ * cached prior into the workspace (code * scale rounded once to bf16, 1 KiB
+ * per token: every position before the chunk on a global layer, the
+ * 2048-slot ring on a local one) and runs the bf16 prefill on it; ws must
+ * hold gqa_workspace_bytes(GQA_OP_PREFILL_FP8, kind, B, n, max pos0 + n)
+ * bytes; errors as gqa_attn_prefill.
  * Pages: runtimewire.com "Long context still costs compute" and "Narrow
  * cache". */
 int gqa_attn_prefill_fp8(const gqa_layer_fp8* layer, const void* q,

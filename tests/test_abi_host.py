@@ -393,17 +393,21 @@ def test_fp8_block_validation(lib, fn):
     op = {"gqa_attn_verify_fp8": ga.OP_VERIFY,
           "gqa_attn_draft_block_fp8": ga.OP_DRAFT,
           "gqa_attn_prefill_fp8": ga.OP_PREFILL}[fn]
+    if fn == "gqa_attn_prefill_fp8":
+        op = ga.OP_PREFILL_FP8
     need = ga.workspace_bytes(op, ga.GLOBAL, 1, 16, 4096)
-    if fn != "gqa_attn_prefill_fp8":
-        assert call(pos=_pos(4080), ws_bytes=need - 1) == E_WS
-    else:
-        # fp8 prefill keeps no partial sums; the query covers the bf16 call's
-        assert call(pos=_pos(4080), ws_bytes=255) == E_WS
+    assert call(pos=_pos(4080), ws_bytes=need - 1) == E_WS
     if fn == "gqa_attn_draft_block_fp8":
         assert call(layer=_layer8(kind=ga.LOCAL)) == E_UNS
     elif fn == "gqa_attn_prefill_fp8":
+        # the bf16 prefill's workspace plus a bf16 copy of the prior
+        # (1 KiB per token: positions before the chunk, or the ring)
+        bf = ga.workspace_bytes(ga.OP_PREFILL, ga.GLOBAL, 1, 16, 4096)
+        assert need >= bf + (4096 - 1) * 1024
+        loc = ga.workspace_bytes(op, ga.LOCAL, 1, 16, 4096)
+        assert loc >= 2048 * 1024
         assert call(layer=_layer8(kind=ga.LOCAL), pos=_pos(4080),
-                    ws_bytes=255) == E_WS
+                    ws_bytes=loc - 1) == E_WS
     else:
         # the local workspace query covers the fp8 call's key splits
         need = ga.workspace_bytes(op, ga.LOCAL, 1, 16, 4096)

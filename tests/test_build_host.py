@@ -34,13 +34,13 @@ def test_parse_and_reject():
 
 
 def test_library_kernels_use_no_private_memory(tmp_path):
-    """The append kernels compiled as the build compiles them (the build
-    applies the same check to every source)."""
+    """The append kernels and the fp8-to-bf16 copy compiled as the build
+    compiles them (the build applies the same check to every source)."""
     src = os.path.join(b.CSRC, "kv_append.hip")
     r = subprocess.run([b.HIPCC] + b.COMMON + b.DEVICE + b.RESOURCES +
                        ["-c", src, "-o", str(tmp_path / "a.o")],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     res = b.kernel_resources(r.stderr)
-    assert len(res) == 2, res
+    assert len(res) == 3, res
     b.check_resources(res, src)

@@ -31,9 +31,9 @@ void shim_plan_decode(int kind, int B, long long keys, int cus, int xcds,
   out[3] = (long long)decode_ws_bytes(B, p);
 }
 void shim_plan_block(int kind, int B, int n, long long keys, int cus,
-                     int xcds, int fp8, long long* out) {
+                     int xcds, int always_split, long long* out) {
   const BlockPlan p = plan_block(kind, B, n, keys, DeviceShape{cus, xcds},
-                                 static_cast<BlockFp8>(fp8));
+                                 always_split != 0);
   out[0] = p.qpw;
   out[1] = p.qgroups;
   out[2] = p.splits;
@@ -72,11 +72,10 @@ def plans(tmp_path_factory):
         lib.shim_plan_decode(kind, B, keys, cus, xcds, out)
         return dict(zip(("splits", "tps", "hpw", "ws"), out))
 
-    def block(kind, B, n, keys, cus, xcds=8, always_split=False,
-              walk8=False):
+    def block(kind, B, n, keys, cus, xcds=8, always_split=False):
         out = (ll * 8)()
-        fp8 = 1 if always_split else 2 if walk8 else 0
-        lib.shim_plan_block(kind, B, n, keys, cus, xcds, fp8, out)
+        lib.shim_plan_block(kind, B, n, keys, cus, xcds, int(always_split),
+                            out)
         return dict(zip(("qpw", "qgroups", "splits", "grid", "walks", "klin",
                          "part", "ws"), out))
     return decode, block
@@ -211,22 +210,3 @@ def test_block_plans_always_split(plans, cus, xcds):
                 assert p["part"] >= groups * p["splits"] * qpw * 16 * 272
                 assert p["ws"] >= p["part"]
 
-
-@pytest.mark.parametrize("cus,xcds", SHAPES)
-def test_block_plans_fp8_prefill(plans, cus, xcds):
-    """Prefill over fp8 caches: never key splits (each workgroup walks its
-    items), 8-token workgroups on both kinds, no rotated-key copy."""
-    _, block = plans
-    for kind in (LOCAL, GLOBAL):
-        for B in (1, 4):
-            for n, ctx in ((1, 100), (100, 5000), (4096, 4096),
-                           (4096, 131072)):
-                keys = min(ctx, W) if kind == LOCAL else ctx
-                p = block(kind, B, n, keys, cus, xcds, walk8=True)
-                qpw = 8
-                assert p["qpw"] == qpw and p["splits"] == 1
-                assert p["klin"] == 0 and p["part"] == 0
-                items = -(-n // qpw) * 2 * B
-                assert p["grid"] <= cus
-                assert p["grid"] * p["walks"] >= items
-                assert (p["grid"] - 1) * p["walks"] < items
