@@ -306,9 +306,7 @@ static int block_launch(const gqa_layer* layer, const void* q,
                         const void* k_blk, const void* v_blk,
                         const int64_t* pos0, int B, int n, void* out,
                         void* ws, size_t ws_bytes, bool verify, bool together,
-                        int64_t max_keys, const BlockPlan& plan,
-                        void* stream) {
-  (void)max_keys;
+                        const BlockPlan& plan, void* stream) {
   if (!ws) return GQA_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return GQA_ERR_MISALIGNED;
   if (ws_bytes < block_ws_bytes(plan)) return GQA_ERR_WS_TOO_SMALL;
@@ -358,7 +356,7 @@ static int block_impl(const gqa_layer* layer, const void* q,
   const BlockPlan plan =
       plan_block(layer->kind, B, n, max_keys, current_device_shape());
   return block_launch(layer, q, k_blk, v_blk, pos0, B, n, out, ws, ws_bytes,
-                      verify, together, max_keys, plan, stream);
+                      verify, together, plan, stream);
 }
 
 int gqa_attn_verify(const gqa_layer* layer, const void* q, const void* k_blk,
@@ -492,8 +490,7 @@ int gqa_attn_prefill_fp8(const gqa_layer_fp8* layer, const void* q,
   view.v = d.v_out;
   view.seq_stride = d.out_stride;
   return block_launch(&view, q, k_chunk, v_chunk, pos0, B, n, out, ws,
-                      lay.block_bytes, false, false, max_keys, lay.plan,
-                      stream);
+                      lay.block_bytes, false, false, lay.plan, stream);
 }
 
 int gqa_attn_prefill(const gqa_layer* layer, const void* q,
