@@ -12,6 +12,8 @@ and edge rows of the last 4096-token chunk of 131072), ragged batches (an empty 
 local window that wraps the ring), the full 131056-token prior, needles at
 key-split and tile edges and inside the block, the drafted block predicted
 together, and an exactly held cache against the bf16 verification."""
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -190,3 +192,86 @@ def test_prefill_fp8_last_chunk_131072_sampled(kind):
                         else None)
     check_close(got, want, "prefill fp8 131072 kind=%d" % kind,
                 ctx=ga.MAX_CONTEXT if kind == ga.GLOBAL else ga.WINDOW)
+
+
+def _random_cases(count=48):
+    rng = random.Random(20261204)
+    out = []
+    for _ in range(count):
+        op = rng.choice(["verify", "draft", "prefill"])
+        kind = ga.GLOBAL if op == "draft" else rng.choice([ga.LOCAL, ga.GLOBAL])
+        B = rng.randint(1, 4)
+        n = rng.randint(1, 16) if op != "prefill" else rng.randint(1, 600)
+        pos0 = [rng.choice([rng.randint(0, 100), rng.randint(0, 12000)])
+                for _ in range(B)]
+        rows = (list(range(n)) if n <= 48 else sorted(
+            set([0, 1, n - 2, n - 1] + rng.sample(range(n), 40))))
+        out.append((op, kind, pos0, n, rng.randint(1, 10 ** 6), rows))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(),
+                         ids=lambda c: "%s-%d" % (c[0], c[1]))
+def test_fp8_block_random_case(case):
+    """Randomly drawn shapes (fixed seed) of the three calls over the fp8
+    cache: ragged batches of 1-4 sequences mixing short (< 100) and long (up
+    to 12000) priors, 1-16 block tokens, 1-600 prefill tokens (prefill:
+    first two, last two and 40 sampled rows)."""
+    op, kind, pos0, n, seed, rows = case
+    got, want, _ = _run(kind, pos0, n, seed, together=op == "draft",
+                        prefill=op == "prefill", rows=rows)
+    check_close(got, want, "fp8 %s kind=%d pos0=%s n=%d seed=%d" %
+                (op, kind, pos0, n, seed))
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_fp8_block_calls_in_a_graph(kind):
+    """Verification and prefill over the fp8 cache captured in a HIP graph:
+    every replay, with eager work and synchronisation between replays,
+    equals the eager call bit for bit."""
+    pos0, n, npf = [3000, 700], 16, 300
+    B = len(pos0)
+    streams = [si.stream(si.seq_seed(8271, b), pos0[b] + npf)
+               for b in range(B)]
+    cap = None if kind == ga.LOCAL else 4096
+    layer, _ = _fill_prior(kind, streams, pos0, cap)
+    dev = "cuda"
+    qv = torch.stack([si.queries(si.seq_seed(8271, b) + 1, n)
+                      for b in range(B)]).to(dev)
+    qp = torch.stack([si.queries(si.seq_seed(8271, b) + 2, npf)
+                      for b in range(B)]).to(dev)
+    kv = torch.stack([streams[b][0][pos0[b]:pos0[b] + npf]
+                      for b in range(B)]).to(dev)
+    vv = torch.stack([streams[b][1][pos0[b]:pos0[b] + npf]
+                      for b in range(B)]).to(dev)
+    kb, vb = kv[:, :n].contiguous(), vv[:, :n].contiguous()
+    ctx = max(pos0) + npf
+    wsv = ga.workspace(ga.OP_VERIFY, kind, B, n, ctx)
+    wsp = ga.workspace(ga.OP_PREFILL_FP8, kind, B, npf, ctx)
+    ov = torch.empty(B, n, ga.HQ, ga.D, dtype=torch.float32, device=dev)
+    op = torch.empty(B, npf, ga.HQ, ga.D, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ga.attn_verify_fp8(layer, qv, kb, vb, pos0, ov, wsv)
+        ga.attn_prefill_fp8(layer, qp, kv, vv, pos0, op, wsp)
+
+    step()
+    torch.cuda.synchronize()
+    ref_v, ref_p = ov.clone(), op.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        ov.zero_()
+        op.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ov, ref_v), "verify replay %d" % rep
+        assert torch.equal(op, ref_p), "prefill replay %d" % rep
