@@ -440,8 +440,52 @@ def bench_draft(ga, torch, layers, kinds, B, n_drafter=5, reps=5, seed=4404):
                         "context, batch %d" % (len(glob), B)}
 
 
+def prefill_oracle_sample(ga, torch, kind, q, k, v, out, c0, nrows,
+                          seed=5115):
+    """The fp64 oracle on this host for `nrows` randomly drawn rows of the
+    last prefill chunk (positions c0 ..), each checked against the GPU's
+    bf16 output of that chunk (max abs <= 2e-2, mean abs <= 2e-3; a miss
+    raises).  Returns the oracle's rate over the sample."""
+    import numpy as np
+    import oracle
+    import synth_inputs as si
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    n = out.shape[1]
+    rows = np.sort(np.random.default_rng(seed).choice(n, nrows,
+                                                      replace=False))
+    pos = c0 + rows
+    lo = 0 if kind == ga.GLOBAL else max(0, c0 - ga.WINDOW + 1)
+    kb = si.bits(k[0, lo:c0 + n])
+    vb = si.bits(v[0, lo:c0 + n])
+    qb = si.bits(q[0, torch.as_tensor(c0 + rows, device=q.device)])
+    ts = time.perf_counter()
+    want = oracle.attend(qb, pos, kb, vb, lo, hq=32, hkv=2, d=128,
+                         window=ga.WINDOW if kind == ga.LOCAL else 0,
+                         rope=kind == ga.LOCAL, nthreads=cores)
+    elapsed = time.perf_counter() - ts
+    got = out[0, torch.as_tensor(rows, device=out.device)].float().cpu() \
+        .double().numpy()
+    err = np.abs(got - want)
+    if not (err.max() <= 2e-2 and err.mean() <= 2e-3):
+        raise RuntimeError("prefill rows differ from the oracle: max abs "
+                           "%.3e, mean abs %.3e" % (err.max(), err.mean()))
+    pairs = int(sum(p + 1 - max(lo, p - ga.WINDOW + 1 if kind == ga.LOCAL
+                                else 0) for p in pos))
+    flops = pairs * 4 * ga.HQ * ga.D
+    return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": "fp64 oracle, %d random rows of the last %d-token "
+                      "chunk (positions %d..), %.3g flop in %.2f s; the "
+                      "GPU's rows match it (max abs %.2e, mean abs %.2e)" %
+                      (nrows, n, c0, flops, elapsed, err.max(), err.mean())}
+
+
 def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005,
-                  fp8=False):
+                  fp8=False, with_oracle=True):
     """Chunked causal prefill of `total` tokens in `chunk`-token chunks on
     one local and one global layer: prefill then append per chunk (fp8:
     over fp8 caches, appending with the quantiser)."""
@@ -485,13 +529,18 @@ def bench_prefill(ga, torch, chunk=4096, total=CTX, reps=1, seed=5005,
                      "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
                                         MFMA_PEAK_TFLOPS, 4),
                      "algorithmic_flop": flops}
+        if not fp8 and with_oracle:
+            res[name]["cpu_baseline"] = prefill_oracle_sample(
+                ga, torch, kind, q, k, v, out, total - chunk,
+                64 if kind == ga.GLOBAL else 512)
         del q, k, v, layer, ws, out
         torch.cuda.empty_cache()
     res["workload"] = ("prefill of %d tokens in %d-token chunks (prefill + "
                        "append per chunk), batch 1%s" %
                        (total, chunk, ", over fp8 caches" if fp8 else ""))
     if not fp8:
-        res["fp8"] = bench_prefill(ga, torch, chunk, total, reps, seed, True)
+        res["fp8"] = bench_prefill(ga, torch, chunk, total, reps, seed, True,
+                                   False)
     return res
 
 
@@ -599,7 +648,8 @@ def main():
     ga = _ensure_built()
     torch.cuda.set_device(0)
     if args.prefill_only:
-        print(json.dumps({"prefill": bench_prefill(ga, torch)}), flush=True)
+        print(json.dumps({"prefill": bench_prefill(
+            ga, torch, with_oracle=not args.no_cpu_baseline)}), flush=True)
         return
     if args.calibrate_copy_mib:
         nbytes = args.calibrate_copy_mib << 20
@@ -694,7 +744,8 @@ def main():
         torch.cuda.empty_cache()
         line["decode_b1"] = bench_decode_b1(ga, torch, args.steps, args.warmup)
         print("# single-sequence decode done", file=sys.stderr, flush=True)
-        line["prefill"] = bench_prefill(ga, torch)
+        line["prefill"] = bench_prefill(
+            ga, torch, with_oracle=not args.no_cpu_baseline)
         print("# prefill done", file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
