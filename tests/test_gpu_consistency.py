@@ -168,3 +168,41 @@ def test_verify_max_batch_64(kind):
     want = _oracle_rows(kind, q[sample], [streams[b] for b in sample],
                         [pos0[b] for b in sample], list(range(n)))
     check_close(got[sample], want, "verify B=64 kind=%d" % kind)
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_prefill_max_batch_64(kind):
+    """Prefill of 100 tokens for 64 sequences at ragged positions (an empty
+    prior first, a wrapped local ring last); every row of five sequences."""
+    rng = np.random.default_rng(4040 + kind)
+    pos0 = [int(x) for x in rng.integers(0, 5000, 64)]
+    pos0[0], pos0[-1] = 0, 4900
+    n = 100
+    print("prefill B=64 kind=%d" % kind, flush=True)
+    layer, streams, q, kb, vb = _setup(kind, pos0, n, seed=4041 + kind)
+    out = ga.attn_prefill(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    sample = [0, 1, 17, 40, 63]
+    want = _oracle_rows(kind, q[sample], [streams[b] for b in sample],
+                        [pos0[b] for b in sample], list(range(n)))
+    check_close(got[sample], want, "prefill B=64 kind=%d" % kind)
+
+
+def test_draft_block_max_batch_64():
+    """A drafted block of 16 tokens predicted together for 64 sequences at
+    ragged positions; five sequences checked against the oracle."""
+    from tests.test_gpu_draft import _oracle_together
+    rng = np.random.default_rng(4050)
+    pos0 = [int(x) for x in rng.integers(0, 5000, 64)]
+    pos0[0], pos0[-1] = 0, 4984
+    n = 16
+    print("draft B=64", flush=True)
+    layer, streams, q, kb, vb = _setup(ga.GLOBAL, pos0, n, seed=4051)
+    out = ga.attn_draft_block(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    sample = [0, 1, 17, 40, 63]
+    want = _oracle_together(q[sample], [streams[b] for b in sample],
+                            [pos0[b] for b in sample], n)
+    check_close(got[sample], want, "draft B=64")

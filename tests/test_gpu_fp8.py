@@ -15,6 +15,8 @@ of the GPU's cache feeds the expected values), max abs <= 2e-2 and mean abs
 <= 2e-3, at context 4096, ragged batches across tile and ring edges, the full
 131072 context, a zero query (exact mean of the dequantised values), constant
 V and needles."""
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -177,6 +179,18 @@ def test_decode_fp8_ragged(kind):
                  4095, 5001]
     got, want, _ = _case(kind, positions, 8102)
     check_close(got, want, "decode fp8 ragged kind=%d" % kind)
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_decode_fp8_max_batch_64(kind):
+    """The largest batch the library takes: 64 sequences at ragged positions
+    0 .. 2999 (position 0 first, a wrapped local ring last)."""
+    rng = random.Random(8111 + kind)
+    positions = [rng.randrange(0, 3000) for _ in range(ga.MAX_BATCH)]
+    positions[0], positions[-1] = 0, 2999
+    got, want, _ = _case(kind, positions, 8111,
+                         capacity=3008 if kind == ga.GLOBAL else None)
+    check_close(got, want, "decode fp8 B=64 kind=%d" % kind)
 
 
 @pytest.mark.parametrize("kind,positions", [

@@ -8,10 +8,11 @@ values, the block's own tokens (which arrive with the call, not yet in the
 cache) at their bf16 values.  Bar: max abs <= 2e-2, mean abs <= 2e-3, and the
 max/RMS gate beyond 32K keys.  Covered: both layer kinds, blocks of 1, 5 and
 16 tokens, prefill chunks (every row of chunks up to 2500 tokens, sampled
-and edge rows of the last 4096-token chunk of 131072), ragged batches (an empty prior, a prior shorter than a tile, a
-local window that wraps the ring), the full 131056-token prior, needles at
-key-split and tile edges and inside the block, the drafted block predicted
-together, and an exactly held cache against the bf16 verification."""
+and edge rows of the last 4096-token chunk of 131072), ragged batches (an
+empty prior, a prior shorter than a tile, a local window that wraps the
+ring), the largest batch (64 sequences), the full 131056-token prior,
+needles at key-split and tile edges and inside the block, the drafted block
+predicted together, and an exactly held cache against the bf16 verification."""
 import random
 
 import numpy as np
@@ -222,6 +223,23 @@ def test_fp8_block_random_case(case):
                         prefill=op == "prefill", rows=rows)
     check_close(got, want, "fp8 %s kind=%d pos0=%s n=%d seed=%d" %
                 (op, kind, pos0, n, seed))
+
+
+@pytest.mark.parametrize("op,kind", [
+    ("verify", ga.LOCAL), ("verify", ga.GLOBAL), ("draft", ga.GLOBAL),
+    ("prefill", ga.LOCAL), ("prefill", ga.GLOBAL)])
+def test_fp8_block_max_batch_64(op, kind):
+    """The largest batch the library takes (64 sequences), ragged priors of
+    0 to 3000 tokens (an empty prior first, a wrapped local ring last):
+    verification and the drafted block with 16 tokens, prefill with 100
+    (every row)."""
+    rng = random.Random(8290 + kind)
+    pos0 = [rng.randrange(0, 3000) for _ in range(ga.MAX_BATCH)]
+    pos0[0], pos0[-1] = 0, 2999
+    n = 100 if op == "prefill" else 16
+    got, want, _ = _run(kind, pos0, n, 8290 + kind, together=op == "draft",
+                        prefill=op == "prefill")
+    check_close(got, want, "fp8 %s B=64 kind=%d" % (op, kind))
 
 
 @pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
