@@ -10,7 +10,8 @@ chunk of 131072) are checked on sampled rows plus the edge rows.  At full
 size the prefill also has gates a tolerance alone would miss there: a zero
 query on every row of the last chunk against the exact mean of its visible
 values, needles at the prior's ends, a tile edge, the causal diagonal and
-the window edge, and every row of the first chunk."""
+the window edge, and every row of the first chunk; the whole prompt in one
+131072-token chunk is checked on sampled rows."""
 import numpy as np
 import pytest
 import torch
@@ -367,3 +368,25 @@ def test_prefill_first_chunk_every_row(kind):
     want = _oracle_rows(kind, q, streams, pos0, list(range(n)))
     check_close(out.float().cpu().numpy(), want,
                 "prefill chunk 0 kind=%d (all rows)" % kind)
+
+
+@pytest.mark.parametrize("kind", [ga.LOCAL, ga.GLOBAL])
+def test_prefill_one_chunk_of_131072(kind):
+    """The largest chunk the library takes: the whole 131072-token prompt in
+    one call from an empty cache, checked on the edge rows, the last rows and
+    64 random rows."""
+    pos0, n = [0], ga.MAX_CONTEXT
+    print("prefill one chunk of 131072 kind=%d" % kind, flush=True)
+    layer, streams, q, kb, vb = _setup(kind, pos0, n, seed=3310,
+                                       capacity=n if kind == ga.GLOBAL
+                                       else None)
+    out = ga.attn_prefill(layer, q.cuda(), kb.cuda(), vb.cuda(), pos0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = sorted(set(_edge_rows(n) + [n - 4097, n - 4096] +
+                      [int(x) for x in rng.choice(n, 64, replace=False)]))
+    want = _oracle_rows(kind, q, streams, pos0, rows)
+    got = out[:, rows].float().cpu().numpy()
+    check_close(got, want, "prefill one chunk of 131072 kind=%d (%d rows)" %
+                (kind, len(rows)),
+                ctx=131072 if kind == ga.GLOBAL else ga.WINDOW)
